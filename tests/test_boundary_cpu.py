@@ -1,0 +1,111 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+symbol declared in include/convrot.h, and rejects bad arguments with the
+documented status codes before anything is launched."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convrot.h")
+
+
+@pytest.fixture(scope="module")
+def cr():
+    import w8a8_rotated_int8_amd as cr
+    if not os.path.exists(cr.library_path):
+        from w8a8_rotated_int8_amd import build
+        build.build()
+    cr.lib()
+    return cr
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(convrot_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    syms = declared_symbols()
+    for s in ("convrot_quantize_weight", "convrot_linear_fwd", "convrot_linear_bwd_dx",
+              "convrot_embedding_lookup"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(cr):
+    L = C.CDLL(cr.library_path)
+    syms = declared_symbols()
+    assert len(syms) >= 11
+    for s in syms:
+        assert hasattr(L, s), s
+    assert sorted(cr.EXPORTS) == syms
+
+
+def test_status_strings(cr):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert cr.status_string(code) != "unknown status"
+    assert cr.status_string(7) == "unknown status"
+
+
+def test_workspace_sizes(cr):
+    M, N, K = 4096, 4096, 4096
+    assert cr.workspace_bytes(cr.OP_LINEAR_FWD, M, N, K) == M * K + 4 * M
+    assert cr.workspace_bytes(cr.OP_LINEAR_BWD_DX, M, N, K, cr.BWD_INT8) == M * N + 4 * M
+    assert cr.workspace_bytes(cr.OP_LINEAR_BWD_DX, M, N, K, cr.BWD_BF16) == 2 * N * K
+    assert cr.workspace_bytes(cr.OP_LINEAR_FWD, 0, N, K) == 0
+    assert cr.workspace_bytes(9, M, N, K) == 0
+
+
+# Fake, well-aligned, never-dereferenced device addresses: validation must reject
+# these calls before any HIP call or launch.
+A = C.c_void_p(1 << 20)
+B = C.c_void_p(2 << 20)
+Y = C.c_void_p(3 << 20)
+WS = C.c_void_p(4 << 20)
+
+
+def test_null_pointers_are_einval(cr):
+    L = cr.lib()
+    assert L.convrot_linear_fwd(None, 4, 128, B, B, 4, None, Y, WS, 1 << 20, None) == -1
+    assert L.convrot_quantize_weight(None, 4, 128, 128, 0, B, Y, None) == -1
+    assert L.convrot_embedding_lookup(None, 4, B, B, 10, 128, Y, None, None) == -1
+    assert L.convrot_linear_bwd_dx(A, 4, 128, None, B, 128, 0, Y, WS, 1 << 20, None) == -1
+
+
+def test_bad_sizes_and_shapes(cr):
+    L = cr.lib()
+    assert L.convrot_linear_fwd(A, 0, 128, B, B, 4, None, Y, WS, 1 << 20, None) == -1
+    assert L.convrot_linear_fwd(A, 4, 100, B, B, 4, None, Y, WS, 1 << 20, None) == -2
+    assert L.convrot_linear_fwd(A, 4, 128 * 257, B, B, 4, None, Y, WS, 1 << 30, None) == -2
+    assert L.convrot_quantize_weight(A, 4, 128, 64, 0, B, Y, None) == -2
+    assert L.convrot_quantize_weight(A, 4, 130, 128, 0, B, Y, None) == -2
+    assert L.convrot_embedding_lookup(A, 4, B, B, 10, 96, Y, None, None) == -2
+    assert L.convrot_linear_bwd_dx(A, 4, 100, B, B, 128, 0, Y, WS, 1 << 20, None) == -2
+    assert L.convrot_linear_bwd_dx(A, 4, 128, B, B, 128, 2, Y, WS, 1 << 20, None) == -1
+    assert L.convrot_gemm_i8_i32(A, B, 4, 100, 128, 1, Y, None) == -2
+    assert L.convrot_gemm_i8_i32(A, B, 4, 100, 128, 3, Y, None) == -1
+
+
+def test_misalignment_is_einval(cr):
+    L = cr.lib()
+    odd = C.c_void_p((1 << 20) + 2)
+    assert L.convrot_linear_fwd(odd, 4, 128, B, B, 4, None, Y, WS, 1 << 20, None) == -1
+    ws_odd = C.c_void_p((4 << 20) + 16)
+    assert L.convrot_linear_fwd(A, 4, 128, B, B, 4, None, Y, ws_odd, 1 << 20, None) == -1
+
+
+def test_workspace_too_small(cr):
+    L = cr.lib()
+    need = cr.workspace_bytes(cr.OP_LINEAR_FWD, 64, 256, 256)
+    assert L.convrot_linear_fwd(A, 64, 256, B, B, 256, None, Y, WS, need - 1, None) == -3
+    need = cr.workspace_bytes(cr.OP_LINEAR_BWD_DX, 64, 256, 256, cr.BWD_INT8)
+    assert L.convrot_linear_bwd_dx(A, 64, 256, B, B, 256, 1, Y, WS, need - 1, None) == -3
+
+
+def test_binding_fails_loudly_without_library(cr, monkeypatch, tmp_path):
+    import importlib
+    monkeypatch.setattr(cr, "_lib", None)
+    monkeypatch.setattr(cr, "library_path", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        cr.lib()

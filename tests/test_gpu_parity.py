@@ -1,0 +1,281 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Codes, scales and int32 accumulators must match bit for bit; bf16 outputs must
+be within 1e-2 of the oracle per row (max abs error / max abs reference).
+Small cases are compared element by element in full; the full-size workloads
+are compared in full where the oracle is fast (quantizers) and on seeded
+sampled rows where it is not (GEMM outputs).
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def cr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w8a8_rotated_int8_amd as cr
+    cr.lib()
+    return cr
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.lib()
+    return oracle
+
+
+from gpu_util import (assert_exact, assert_rows_close, bf16_to_dev, bits, host,  # noqa: E402
+                      to_dev)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def crafted_rows(K: int) -> np.ndarray:
+    """Rows that pin the quantizer's corner cases, tiled over all blocks of K."""
+    def tile(entries, scale=1.0):
+        v = np.zeros(K, dtype=np.float32)
+        for b0 in range(0, K, 128):
+            for i, val in entries.items():
+                v[b0 + i] = val * scale
+        return v
+    rows = [
+        np.zeros(K, np.float32),                          # all-zero row
+        tile({0: -253.0, 1: -255.0}),                     # exact tie at 0.5
+        tile({0: 3.0, 1: 1.0}),                           # exact tie at 63.5
+        tile({0: -255.0, 1: -85.0}),                      # division vs reciprocal
+        tile({0: 1.0}),                                   # e0
+        tile({i: 1.0 for i in range(128)}),               # ones
+        tile({1: 1.0}), tile({64: -1.0}),
+        tile({0: 2.0 ** 20, 1: 2.0 ** -10, 77: -3.0}),    # wide but exact spread
+        tile({3: 1e-32, 9: -2e-32}),                      # tiny scale (IEEE division path)
+        tile({5: 1e36, 6: -3e35}),                        # huge scale (IEEE division path)
+    ]
+    return wl.f32_to_bf16_bits(np.stack(rows))
+
+
+# --------------------------------------------------------------------------
+# Quantizer (weights, activations, embedding chunks)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 256), (64, 256), (301, 384), (97, 4096),
+                                 (33, 4224), (16, 12288), (24, 16384), (5, 32768)])
+def test_quantize_act_exact(cr, orc, M, K):
+    say(f"quantize_act M={M} K={K}")
+    x = wl.activations(M, K, max(1, wl.n_outliers(K)), base=M + K)
+    x = np.concatenate([x, crafted_rows(K)])
+    q, s = cr.quantize_act(bf16_to_dev(x))
+    oq, os_, bad = orc.rotate_quantize(x)
+    assert bad == 0
+    assert_exact(host(s), os_, "scales")
+    assert_exact(host(q), oq, "codes")
+
+
+def test_quantize_weight_tiny_and_chunked(cr, orc):
+    t = wl.tiny(0)
+    say("quantize_weight tiny")
+    q, s = cr.quantize_weight(bf16_to_dev(t["w"]))
+    oq, os_, _ = orc.rotate_quantize(t["w"])
+    assert_exact(host(q), oq, "codes")
+    assert_exact(host(s), os_, "scales")
+    for chunk in (1, 7, 100, 256):
+        qc, sc = cr.quantize_weight(bf16_to_dev(t["w"]), chunk_rows=chunk)
+        assert_exact(host(qc), oq, f"codes chunk={chunk}")
+        assert_exact(host(sc), os_, f"scales chunk={chunk}")
+
+
+def test_quantize_is_deterministic(cr):
+    x = bf16_to_dev(wl.activations(512, 4096, 41, base=4))
+    q1, s1 = cr.quantize_act(x)
+    q2, s2 = cr.quantize_act(x)
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
+
+
+# --------------------------------------------------------------------------
+# int32 contraction
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (64, 256, 256), (300, 200, 384), (257, 513, 1024),
+                                   (512, 512, 4096), (33, 700, 16384)])
+def test_gemm_i32_exact(cr, orc, M, N, K):
+    say(f"gemm_i8_i32 b_layout=0 M={M} N={N} K={K}")
+    g = np.random.default_rng(M * 7 + N)
+    a = g.integers(-127, 128, (M, K), dtype=np.int8)
+    b = g.integers(-127, 128, (N, K), dtype=np.int8)
+    acc = cr.gemm_i8_i32(to_dev(a), to_dev(b), 0)
+    assert_exact(host(acc), orc.gemm_i8_i32(a, b), "acc")
+
+
+def test_gemm_i32_extreme_values(cr, orc):
+    M, N, K = 64, 256, 16384
+    a = np.full((M, K), -127, np.int8)
+    b = np.full((N, K), -127, np.int8)
+    b[1::2] = 127
+    acc = cr.gemm_i8_i32(to_dev(a), to_dev(b), 0)
+    assert_exact(host(acc), orc.gemm_i8_i32(a, b), "acc")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (1, 128, 128), (300, 384, 640), (129, 4096, 512)])
+def test_gemm_i32_rows_of_b_exact(cr, orc, M, N, K):
+    # acc[m][n] = sum_k a[m][k] b[k][n]  (the int8 input-gradient contraction)
+    say(f"gemm_i8_i32 b_layout=1 M={M} N={N} K={K}")
+    g = np.random.default_rng(M + N + K)
+    a = g.integers(-127, 128, (M, K), dtype=np.int8)
+    b = g.integers(-127, 128, (K, N), dtype=np.int8)
+    acc = cr.gemm_i8_i32(to_dev(a), to_dev(b), 1)
+    assert_exact(host(acc), orc.gemm_i8_i32_rows_of_b(a, b), "acc")
+
+
+# --------------------------------------------------------------------------
+# Forward
+# --------------------------------------------------------------------------
+
+def _fwd_case(cr, orc, x, w, bias=None, rows=None):
+    qw, sw = cr.quantize_weight(bf16_to_dev(w))
+    y = cr.linear_fwd(bf16_to_dev(x), qw, sw, None if bias is None else bf16_to_dev(bias))
+    oqw, osw, _ = orc.rotate_quantize(w)
+    ref = orc.linear_fwd(x, oqw, osw, bias=bias, rows=rows)
+    yb = bits(y)
+    if rows is not None:
+        yb = yb[rows]
+    return yb, ref
+
+
+def test_linear_fwd_tiny(cr, orc):
+    t = wl.tiny(0)
+    say("linear_fwd tiny")
+    yb, ref = _fwd_case(cr, orc, t["x"], t["w"])
+    assert_rows_close(yb, ref["y"], "y")
+    bias = wl.normal_bf16((t["N"],), 0.5, 0, 9)
+    yb, ref = _fwd_case(cr, orc, t["x"], t["w"], bias=bias)
+    assert_rows_close(yb, ref["y"], "y+bias")
+    # elementwise: one fp32 product chain + bf16 rounding vs one rounding in fp64
+    g = wl.bf16_bits_to_f32(yb).astype(np.float64)
+    r = wl.bf16_bits_to_f32(ref["y"]).astype(np.float64)
+    assert np.all(np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 1e-30)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 128), (5, 130, 256), (300, 260, 384), (257, 1000, 1024)])
+def test_linear_fwd_ragged(cr, orc, M, N, K):
+    say(f"linear_fwd ragged M={M} N={N} K={K}")
+    x = wl.activations(M, K, max(1, K // 100), base=M)
+    w = wl.normal_bf16((N, K), wl.SIGMA_W, M, 1)
+    yb, ref = _fwd_case(cr, orc, x, w)
+    assert_rows_close(yb, ref["y"], "y")
+
+
+def test_linear_fwd_attn_full_size(cr, orc):
+    """The attention-projection workload at full size: all codes and scales
+    exact, int32 accumulators and outputs on 64 seeded rows (incl. both ends)."""
+    a = wl.attn(0)
+    say("linear_fwd attn 4096^3")
+    xd, wd = bf16_to_dev(a["x"]), bf16_to_dev(a["w"])
+    qw, sw = cr.quantize_weight(wd)
+    qx, sx = cr.quantize_act(xd)
+    y = cr.linear_fwd(xd, qw, sw)
+    y2 = cr.linear_fwd(xd, qw, sw)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "forward not deterministic"
+    oqw, osw, bad = orc.rotate_quantize(a["w"])
+    assert bad == 0
+    assert_exact(host(qw), oqw, "q_w")
+    assert_exact(host(sw), osw, "s_w")
+    oqx, osx, bad = orc.rotate_quantize(a["x"])
+    assert bad == 0
+    assert_exact(host(qx), oqx, "q_x")
+    assert_exact(host(sx), osx, "s_x")
+    rows = np.unique(np.concatenate([[0, 1, 4095], np.random.default_rng(0).choice(4096, 61, False)]))
+    acc = cr.gemm_i8_i32(qx, qw, 0)
+    oacc = orc.gemm_i8_i32(oqx, oqw, rows)
+    assert_exact(host(acc)[rows], oacc, "acc (sampled rows)")
+    oy = orc.dequant_epilogue(oacc, osx, osw, rows)
+    e = assert_rows_close(bits(y)[rows], oy, "y (sampled rows)")
+    say(f"  max row relerr {e:.2e}")
+
+
+# --------------------------------------------------------------------------
+# Input gradients
+# --------------------------------------------------------------------------
+
+def _bwd_int8(cr, orc, dy, w, rows=None):
+    qw, sw = cr.quantize_weight(bf16_to_dev(w))
+    oqw, osw, _ = orc.rotate_quantize(w)
+    dyd = bf16_to_dev(dy)
+    qg, sg = cr.bwd_quant_dy(dyd, sw)
+    dx = cr.linear_bwd_dx(dyd, qw, sw, cr.BWD_INT8)
+    oqg, osg = orc.bwd_quant_dy(dy, osw)
+    assert_exact(host(sg), osg, "s_g")
+    assert_exact(host(qg), oqg, "q_g")
+    acc2 = cr.gemm_i8_i32(qg, qw, 1)
+    oacc2 = orc.gemm_i8_i32_rows_of_b(oqg, oqw, rows)
+    g = host(acc2) if rows is None else host(acc2)[rows]
+    assert_exact(g, oacc2, "acc2")
+    odx = orc.bwd_int8_epilogue(oacc2, osg, rows)
+    dxb = bits(dx) if rows is None else bits(dx)[rows]
+    return assert_rows_close(dxb, odx, "dX int8")
+
+
+def _bwd_bf16(cr, orc, dy, w, rows=None):
+    qw, sw = cr.quantize_weight(bf16_to_dev(w))
+    oqw, osw, _ = orc.rotate_quantize(w)
+    wt = cr.dequant_weight_t(qw, sw)
+    owhat = orc.dequant_weight(oqw, osw)
+    assert_rows_close(bits(wt), np.ascontiguousarray(owhat.T), "W_hat^T")
+    dx = cr.linear_bwd_dx(bf16_to_dev(dy), qw, sw, cr.BWD_BF16)
+    odx = orc.bf16_gemm_dx(dy, owhat, rows)
+    dxb = bits(dx) if rows is None else bits(dx)[rows]
+    return assert_rows_close(dxb, odx, "dX bf16")
+
+
+def test_bwd_int8_tiny(cr, orc):
+    t = wl.tiny(0)
+    say("bwd int8 tiny")
+    _bwd_int8(cr, orc, t["dy"], t["w"])
+
+
+def test_bwd_bf16_tiny(cr, orc):
+    t = wl.tiny(0)
+    say("bwd bf16 tiny")
+    _bwd_bf16(cr, orc, t["dy"], t["w"])
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (300, 384, 640), (257, 1024, 512)])
+def test_bwd_ragged(cr, orc, M, N, K):
+    say(f"bwd ragged M={M} N={N} K={K}")
+    dy = wl.normal_bf16((M, N), wl.SIGMA_DY, M, 3)
+    dy[0] = 0  # an all-zero gradient row
+    w = wl.normal_bf16((N, K), wl.SIGMA_W, M, 1)
+    _bwd_int8(cr, orc, dy, w)
+    _bwd_bf16(cr, orc, dy, w)
+
+
+# --------------------------------------------------------------------------
+# Embedding
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("V,D,T", [(1000, 4096, 300), (77, 384, 50), (10, 128, 7), (300, 8192, 40)])
+def test_embedding_lookup(cr, orc, V, D, T):
+    say(f"embedding V={V} D={D} T={T}")
+    E = wl.normal_bf16((V, D), wl.SIGMA_W, V, 1)
+    qe, se = cr.quantize_weight(bf16_to_dev(E), chunk_rows=64)
+    oqe, ose, _ = orc.rotate_quantize(E, chunk_rows=64)
+    assert_exact(host(qe), oqe, "q_E")
+    assert_exact(host(se), ose, "s_E")
+    ids = wl.token_ids(T, V, base=D)
+    ids[0], ids[-1] = -5, V   # out of range -> zero rows, counted
+    oob = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = cr.embedding_lookup(to_dev(ids), qe, se, oob)
+    oout, ooob = orc.embedding_lookup(ids, oqe, ose)
+    assert int(oob.item()) == ooob == 2
+    ob = bits(out)
+    assert not ob[0].any() and not ob[-1].any()
+    assert_rows_close(ob, oout, "lookup")

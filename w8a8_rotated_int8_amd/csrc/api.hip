@@ -1,0 +1,212 @@
+// C ABI of libconvrot.so: argument validation, workspace layout and launches.
+// Declarations and the contract of every entry point are in include/convrot.h.
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/convrot.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace convrot {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CONVROT_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return CONVROT_EDEVICE;
+  int st = g_device_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return CONVROT_EHIP;
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_device_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? CONVROT_OK : CONVROT_EDEVICE;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONVROT_EHIP; }
+
+bool row_len_ok(int64_t K) { return K > 0 && K % kBlock == 0 && K <= CONVROT_MAX_ROW_LEN; }
+
+int quantize_rows_checked(const uint16_t* x, int64_t rows, int64_t K, int8_t* q, float* s,
+                          int64_t chunk_rows, const float* colscale, bool fold,
+                          hipStream_t stream) {
+  if (!x || !q || !s || rows <= 0 || K <= 0 || chunk_rows < 0) return CONVROT_EINVAL;
+  if (fold && !colscale) return CONVROT_EINVAL;
+  if (!aligned16(x) || !aligned16(q) || (colscale && !aligned16(colscale))) return CONVROT_EINVAL;
+  if (!row_len_ok(K)) return CONVROT_ESHAPE;
+  int st = check_device();
+  if (st) return st;
+  if (chunk_rows == 0 || chunk_rows > rows) chunk_rows = rows;
+  for (int64_t r0 = 0; r0 < rows; r0 += chunk_rows) {
+    int64_t n = rows - r0 < chunk_rows ? rows - r0 : chunk_rows;
+    hipError_t e = launch_rotate_quant(x + r0 * K, n, (int)K, q + r0 * K, s + r0, colscale, fold,
+                                       stream);
+    if (e != hipSuccess) return CONVROT_EHIP;
+  }
+  return CONVROT_OK;
+}
+
+size_t fwd_workspace(int64_t M, int64_t K) { return align256((size_t)M * K) + align256(4 * (size_t)M); }
+size_t bwd_int8_workspace(int64_t M, int64_t N) {
+  return align256((size_t)M * N) + align256(4 * (size_t)M);
+}
+size_t bwd_bf16_workspace(int64_t N, int64_t K) { return align256(2 * (size_t)N * K); }
+
+}  // namespace
+}  // namespace convrot
+
+using namespace convrot;
+
+extern "C" {
+
+const char* convrot_status_string(int status) {
+  switch (status) {
+    case CONVROT_OK: return "ok";
+    case CONVROT_EINVAL: return "invalid argument (null pointer, non-positive size or misaligned pointer)";
+    case CONVROT_ESHAPE: return "unsupported shape (block must be 128; contraction length a multiple of 128 within limits)";
+    case CONVROT_EWORKSPACE: return "workspace too small";
+    case CONVROT_EHIP: return "HIP runtime or launch error";
+    case CONVROT_EDEVICE: return "current device is not gfx950";
+    default: return "unknown status";
+  }
+}
+
+size_t convrot_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t mode) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  if (op == CONVROT_OP_LINEAR_FWD) return fwd_workspace(M, K);
+  if (op == CONVROT_OP_LINEAR_BWD_DX) {
+    if (mode == CONVROT_BWD_INT8) return bwd_int8_workspace(M, N);
+    if (mode == CONVROT_BWD_BF16) return bwd_bf16_workspace(N, K);
+  }
+  return 0;
+}
+
+int convrot_quantize_weight(const uint16_t* w, int64_t rows, int64_t cols, int32_t block,
+                            int64_t chunk_rows, int8_t* q, float* scale, hipStream_t stream) {
+  if (block != kBlock) return w && q && scale ? CONVROT_ESHAPE : CONVROT_EINVAL;
+  return quantize_rows_checked(w, rows, cols, q, scale, chunk_rows, nullptr, false, stream);
+}
+
+int convrot_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* qx, float* sx,
+                         hipStream_t stream) {
+  return quantize_rows_checked(x, M, K, qx, sx, 0, nullptr, false, stream);
+}
+
+int convrot_bwd_quant_dy(const uint16_t* dy, int64_t M, int64_t N, const float* sw, int8_t* qg,
+                         float* sg, hipStream_t stream) {
+  return quantize_rows_checked(dy, M, N, qg, sg, 0, sw, true, stream);
+}
+
+int convrot_gemm_i8_bf16(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw,
+                         int64_t M, int64_t N, int64_t K, const uint16_t* bias, uint16_t* y,
+                         hipStream_t stream) {
+  if (!qx || !sx || !qw || !sw || !y || M <= 0 || N <= 0 || K <= 0) return CONVROT_EINVAL;
+  if (!aligned16(qx) || !aligned16(qw) || !aligned16(y)) return CONVROT_EINVAL;
+  if (K % kBlock) return CONVROT_ESHAPE;
+  int st = check_device();
+  if (st) return st;
+  GemmArgs a{};
+  a.P = qw; a.Q = qx; a.I = N; a.J = M; a.Kc = K; a.ldp = K; a.ldq = K;
+  a.out = y; a.ldo = N; a.si = sw; a.sj = sx; a.bias = bias;
+  return hip_status(launch_gemm_i8(a, kEpiDequantBf16, false, stream));
+}
+
+int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw,
+                       const float* sw, int64_t N, const uint16_t* bias, uint16_t* y,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!x || !qw || !sw || !y || !workspace || M <= 0 || N <= 0 || K <= 0) return CONVROT_EINVAL;
+  if (!aligned16(x) || !aligned16(qw) || !aligned16(y) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return CONVROT_EINVAL;
+  if (!row_len_ok(K)) return CONVROT_ESHAPE;
+  if (workspace_bytes < fwd_workspace(M, K)) return CONVROT_EWORKSPACE;
+  int st = check_device();
+  if (st) return st;
+  int8_t* qx = static_cast<int8_t*>(workspace);
+  float* sx = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + align256((size_t)M * K));
+  hipError_t e = launch_rotate_quant(x, M, (int)K, qx, sx, nullptr, false, stream);
+  if (e != hipSuccess) return CONVROT_EHIP;
+  GemmArgs a{};
+  a.P = qw; a.Q = qx; a.I = N; a.J = M; a.Kc = K; a.ldp = K; a.ldq = K;
+  a.out = y; a.ldo = N; a.si = sw; a.sj = sx; a.bias = bias;
+  return hip_status(launch_gemm_i8(a, kEpiDequantBf16, false, stream));
+}
+
+int convrot_gemm_i8_i32(const int8_t* a_, const int8_t* b, int64_t M, int64_t N, int64_t K,
+                        int32_t b_layout, int32_t* acc, hipStream_t stream) {
+  if (!a_ || !b || !acc || M <= 0 || N <= 0 || K <= 0) return CONVROT_EINVAL;
+  if (!aligned16(a_) || !aligned16(b) || !aligned16(acc)) return CONVROT_EINVAL;
+  if (b_layout != 0 && b_layout != 1) return CONVROT_EINVAL;
+  if (K % kBlock) return CONVROT_ESHAPE;
+  if (b_layout == 1 && N % kBlock) return CONVROT_ESHAPE;
+  int st = check_device();
+  if (st) return st;
+  GemmArgs a{};
+  a.P = b; a.Q = a_; a.I = N; a.J = M; a.Kc = K; a.ldp = b_layout == 0 ? K : N; a.ldq = K;
+  a.out = acc; a.ldo = N;
+  return hip_status(launch_gemm_i8(a, kEpiI32, b_layout == 1, stream));
+}
+
+int convrot_dequant_weight_t(const int8_t* qw, const float* sw, int64_t N, int64_t K,
+                             uint16_t* what_t, hipStream_t stream) {
+  if (!qw || !sw || !what_t || N <= 0 || K <= 0) return CONVROT_EINVAL;
+  if (!aligned16(qw) || !aligned16(what_t)) return CONVROT_EINVAL;
+  if (K % kBlock) return CONVROT_ESHAPE;
+  int st = check_device();
+  if (st) return st;
+  return hip_status(launch_dequant_weight_t(qw, sw, N, K, what_t, stream));
+}
+
+int convrot_linear_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, const int8_t* qw,
+                          const float* sw, int64_t K, int32_t mode, uint16_t* dx,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dy || !qw || !sw || !dx || !workspace || M <= 0 || N <= 0 || K <= 0) return CONVROT_EINVAL;
+  if (mode != CONVROT_BWD_BF16 && mode != CONVROT_BWD_INT8) return CONVROT_EINVAL;
+  if (!aligned16(dy) || !aligned16(qw) || !aligned16(sw) || !aligned16(dx) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return CONVROT_EINVAL;
+  if (K % kBlock || N % kBlock) return CONVROT_ESHAPE;
+  if (mode == CONVROT_BWD_INT8 && N > CONVROT_MAX_ROW_LEN) return CONVROT_ESHAPE;
+  if (workspace_bytes < convrot_workspace_bytes(CONVROT_OP_LINEAR_BWD_DX, M, N, K, mode))
+    return CONVROT_EWORKSPACE;
+  int st = check_device();
+  if (st) return st;
+  if (mode == CONVROT_BWD_INT8) {
+    int8_t* qg = static_cast<int8_t*>(workspace);
+    float* sg = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + align256((size_t)M * N));
+    hipError_t e = launch_rotate_quant(dy, M, (int)N, qg, sg, sw, true, stream);
+    if (e != hipSuccess) return CONVROT_EHIP;
+    GemmArgs a{};
+    a.P = qw; a.Q = qg; a.I = K; a.J = M; a.Kc = N; a.ldp = K; a.ldq = N;
+    a.out = dx; a.ldo = K; a.sj = sg;
+    return hip_status(launch_gemm_i8(a, kEpiInvRotBf16, true, stream));
+  }
+  uint16_t* what_t = static_cast<uint16_t*>(workspace);
+  hipError_t e = launch_dequant_weight_t(qw, sw, N, K, what_t, stream);
+  if (e != hipSuccess) return CONVROT_EHIP;
+  GemmArgs a{};
+  a.P = what_t; a.Q = dy; a.I = K; a.J = M; a.Kc = N; a.ldp = N; a.ldq = N;
+  a.out = dx; a.ldo = K;
+  return hip_status(launch_gemm_bf16(a, stream));
+}
+
+int convrot_embedding_lookup(const int32_t* ids, int64_t T, const int8_t* qe, const float* se,
+                             int64_t V, int64_t D, uint16_t* out, int32_t* oob_count,
+                             hipStream_t stream) {
+  if (!ids || !qe || !se || !out || T <= 0 || V <= 0 || D <= 0) return CONVROT_EINVAL;
+  if (!aligned16(qe) || !aligned16(out)) return CONVROT_EINVAL;
+  if (D % kBlock) return CONVROT_ESHAPE;
+  int st = check_device();
+  if (st) return st;
+  return hip_status(launch_embedding_lookup(ids, T, qe, se, V, D, out, oob_count, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Device-side helpers shared by the ConvRot kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convrot {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 128;  // Hadamard block along the contraction axis
+
+// 1/sqrt(128) in binary64: fl64(sqrt 2) * 2^-4 (exact scaling of a correctly
+// rounded sqrt).  Writing 1.0 / sqrt(128.0) would round twice and land one ulp
+// low, so the literal is spelled out.
+constexpr double kInvSqrt128 = 0x1.6a09e667f3bcdp-4;
+
+// bf16 bit patterns <-> fp32.
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Correctly rounded fp32 quotient r / s for a per-row divisor s with a
+// precomputed inv = RN(1/s) (Markstein's correction step: the residual
+// e = r - q0*s is exact under FMA and q0 + e*inv rounds to RN(r/s)).  Valid
+// whenever s, 1/s and the quotient are normal numbers; callers route rows with
+// extreme scales through the IEEE division instead.  Where the quotient is
+// subnormal its value only ever rounds to the integer 0, so that case is benign.
+__device__ __forceinline__ float quot_rn(float r, float s, float inv) {
+  float q0 = r * inv;
+  float e = __builtin_fmaf(-q0, s, r);
+  return __builtin_fmaf(e, inv, q0);
+}
+
+// Round-half-even of |t| < 2^22 to an integer, returned as the low byte of the
+// bit pattern of t + 1.5*2^23 (the addition itself performs the RNE rounding;
+// in the binade [2^23, 2^24) the low mantissa bits hold the integer in two's
+// complement).
+__device__ __forceinline__ uint32_t rne_low_byte_bits(float t) {
+  return __float_as_uint(t + 12582912.0f);
+}
+
+// Pack the low bytes of four words into one word (byte i from word i).
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2,
+                                                   uint32_t b3) {
+  uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);  // [b0.0, b1.0, 0, 0]
+  uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);  // [b2.0, b3.0, 0, 0]
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);          // [lo.0, lo.1, hi.0, hi.1]
+}
+
+// Exchange with the other half of the wave: vdst's upper 32 lanes swap with
+// src0's lower 32 lanes (v_permlane32_swap).  Returns {vdst', src0'}.
+__device__ __forceinline__ void swap_halves(uint32_t& vdst, uint32_t& src0) {
+  auto r = __builtin_amdgcn_permlane32_swap(vdst, src0, false, false);
+  vdst = r[0];
+  src0 = r[1];
+}
+__device__ __forceinline__ void swap_halves(double& vdst, double& src0) {
+  uint64_t a = __builtin_bit_cast(uint64_t, vdst), b = __builtin_bit_cast(uint64_t, src0);
+  uint32_t alo = (uint32_t)a, ahi = (uint32_t)(a >> 32), blo = (uint32_t)b, bhi = (uint32_t)(b >> 32);
+  swap_halves(alo, blo);
+  swap_halves(ahi, bhi);
+  vdst = __builtin_bit_cast(double, ((uint64_t)ahi << 32) | alo);
+  src0 = __builtin_bit_cast(double, ((uint64_t)bhi << 32) | blo);
+}
+__device__ __forceinline__ void swap_halves(float& vdst, float& src0) {
+  uint32_t a = __float_as_uint(vdst), b = __float_as_uint(src0);
+  swap_halves(a, b);
+  vdst = __uint_as_float(a);
+  src0 = __uint_as_float(b);
+}
+
+// Wave-wide butterfly max over lanes xor `mask` for masks 1..limit/2.
+__device__ __forceinline__ float wave_max_xor(float v, int limit) {
+  for (int o = 1; o < limit; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Wait for all outstanding vector-memory operations of this wave (including
+// loads that write LDS directly).
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16-byte direct global->LDS load: lane i's 16 bytes land at lds_base + 16*i.
+__device__ __forceinline__ void load_lds_16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
+}
+
+}  // namespace convrot

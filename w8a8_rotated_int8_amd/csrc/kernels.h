@@ -1,0 +1,58 @@
+// Internal launchers of the ConvRot kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define CONVROT_MAX_ROW_LEN_BLOCKS 256  // 32768 / 128
+
+namespace convrot {
+
+struct RowPlan {
+  int rows_per_wave;  // rows packed in one wave (short rows), else 1
+  int waves_per_row;  // waves sharing one row (long rows), else 1
+  int threads;        // workgroup size
+};
+
+RowPlan plan_rows(int K);
+
+// Rotate (fold == false) or scale-fold (fold == true, colscale[K]) each row of
+// x [rows, K] and quantize it per row to int8 codes q and fp32 scales.
+hipError_t launch_rotate_quant(const uint16_t* x, int64_t rows, int K, int8_t* q, float* scale,
+                               const float* colscale, bool fold, hipStream_t stream);
+
+// Epilogues of the tiled GEMM out[j][i] = sum_k P[i][k] * Q[j][k].
+enum GemmEpilogue {
+  kEpiI32 = 0,         // int32 out
+  kEpiDequantBf16 = 1, // bf16( fl32(acc) * sj[j] * si[i] (+ bias[i]) )
+  kEpiInvRotBf16 = 2,  // bf16( inverse-rotate along i of fl32(acc) * sj[j] )
+  kEpiBf16 = 3,        // bf16(acc) of an fp32 accumulation
+};
+
+struct GemmArgs {
+  const void* P;      // [I, Kc] row-major, or [Kc, I] when transposed
+  const void* Q;      // [J, Kc] row-major
+  int64_t I, J, Kc;   // Kc in elements
+  int64_t ldp, ldq;   // row strides in elements
+  void* out;          // [J, I] row-major
+  int64_t ldo;
+  const float* si;    // per-i scale (dequant epilogue)
+  const float* sj;    // per-j scale
+  const uint16_t* bias;  // per-i bf16 bias or nullptr
+};
+
+// int8 operands (MFMA i32 32x32x32).  p_transposed: P is given as [Kc, I].
+hipError_t launch_gemm_i8(const GemmArgs& a, int epilogue, bool p_transposed, hipStream_t stream);
+// bf16 operands (MFMA f32 32x32x16), both row-major, kEpiBf16.
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t stream);
+
+// W_hat^T [K, N] bf16 from q_w [N, K], s_w [N].
+hipError_t launch_dequant_weight_t(const int8_t* qw, const float* sw, int64_t N, int64_t K,
+                                   uint16_t* what_t, hipStream_t stream);
+
+// Embedding lookup with row dequantization and inverse rotation.
+hipError_t launch_embedding_lookup(const int32_t* ids, int64_t T, const int8_t* qe,
+                                   const float* se, int64_t V, int64_t D, uint16_t* out,
+                                   int32_t* oob, hipStream_t stream);
+
+}  // namespace convrot
