@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of the ConvRot INT8 linear layer on one MI355X (gfx950).
+
+Headline (one JSON line on stdout): the fused forward ``convrot_linear_fwd``
+(online rotation + per-row activation quantization + int8 MFMA GEMM +
+dequantizing epilogue) on the attention-projection workload, M = K = N = 4096
+tokens x features, in TOPS = 2*M*N*K / wall time per call, with the weight
+quantized beforehand (load time).  A "step" is one such call on inputs already
+resident in HBM.
+
+The same line carries
+  * ``roofline``: the dominant kernel (the int8 GEMM with its epilogue) timed
+    alone with HIP events on its stream, against the 5.0 POP/s dense-int8 MFMA
+    peak; ``traffic`` comes from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counters when they were taken on the current kernel source, else null;
+  * ``cpu_baseline``: the CPU oracle (plain C, OpenMP) on the full forward of
+    the same workload on this host;
+  * ``extra``: the other hot-path kernels on their workloads (load-time and
+    embedding quantizers, lookup, both input-gradient modes, the MLP pair and
+    the 252-linear packed stream).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|all]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+METRIC = "fused ConvRot INT8 linear TOPS (M=K=N=4096) and % of MI355X INT8 MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only", default="all", choices=["all", "fwd", "kernels"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the ConvRot linear runs on a single MI355X here "
+              "(token-parallel sharding needs no collective and is not exercised); "
+              "run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import w8a8_rotated_int8_amd as cr
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cr.lib()
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def time_ms(fn, warmup, iters):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(iters):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / iters
+
+    def dev_normal(shape, sigma, seed, outlier_cols=None):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        v = torch.randn(shape, generator=g, device=dev, dtype=torch.float32)
+        if sigma != 1.0:
+            v.mul_(sigma)
+        if outlier_cols is not None:
+            v[:, torch.from_numpy(outlier_cols).to(dev)] *= wl.OUTLIER_GAIN
+        return v.to(torch.bfloat16)
+
+    # ------------------------------------------------------------------
+    # headline: attention projection, M = K = N = 4096
+    # ------------------------------------------------------------------
+    log("[bench] generating the attention-projection workload (seeded, numpy recipe)")
+    a = wl.attn(0)
+    M, K, N = a["M"], a["K"], a["N"]
+    x = to_dev(a["x"])
+    w = to_dev(a["w"])
+    qw, sw = cr.quantize_weight(w)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(cr.workspace_bytes(cr.OP_LINEAR_FWD, M, N, K), dtype=torch.uint8, device=dev)
+    ops = 2.0 * M * N * K
+
+    def step():
+        cr.linear_fwd(x, qw, sw, out=y, workspace=ws)
+
+    log(f"[bench] headline: {args.warmup} warmup + {args.steps} timed linear_fwd calls")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    tops = ops / (ms_step * 1e-3) / 1e12
+    log(f"[bench] linear_fwd {ms_step * 1e3:.1f} us/call  {tops:.1f} TOPS  "
+        f"({100 * tops / PEAK_INT8_TOPS:.1f}% of int8 peak; host wall {wall * 1e3 / args.steps:.1f} us)")
+
+    # dominant kernel alone: int8 GEMM + dequantizing epilogue
+    qx, sx = cr.quantize_act(x)
+    y2 = torch.empty_like(y)
+    iters = max(args.steps, 100)
+    gemm_ms = time_ms(lambda: cr.gemm_i8_bf16(qx, sx, qw, sw, out=y2), args.warmup, iters)
+    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
+    aq_ms = time_ms(lambda: cr.quantize_act(x), args.warmup, iters)
+    aq_bytes = M * K * 2 + M * K + 4 * M
+    log(f"[bench] gemm kernel {gemm_ms * 1e3:.1f} us ({gemm_tops:.1f} TOPS); act quant "
+        f"{aq_ms * 1e3:.1f} us ({aq_bytes / (aq_ms * 1e-3) / 1e9:.0f} GB/s, MALL-resident)")
+
+    roofline = {
+        "bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+        "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": gemm_traffic(),
+        "kernel": "gemm_kernel<dequant-bf16> (int8 MFMA 32x32x32)", "avg_launch_us": round(gemm_ms * 1e3, 2),
+        "algorithmic_ops_per_launch": ops,
+    }
+
+    extra = {
+        "linear_fwd_us": round(ms_step * 1e3, 2),
+        "linear_fwd_pct_int8_peak": round(100 * tops / PEAK_INT8_TOPS, 2),
+        "gemm_kernel_us": round(gemm_ms * 1e3, 2),
+        "act_quant_us": round(aq_ms * 1e3, 2),
+        "act_quant_GBps_mall_resident": round(aq_bytes / (aq_ms * 1e-3) / 1e9, 1),
+    }
+    wq_ms = time_ms(lambda: cr.quantize_weight(w, out=(qw, sw)), 3, 20)
+    extra["weight_quant_attn_us"] = round(wq_ms * 1e3, 2)
+    del x, w, ws, y, y2, qx, sx
+
+    if args.only == "all":
+        extra.update(bench_embedding(cr, torch, dev, dev_normal, time_ms, wl))
+        extra.update(bench_mlp(cr, torch, dev, dev_normal, time_ms, wl))
+        extra.update(bench_packed(cr, torch, dev, dev_normal, time_ms, wl))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(a)
+
+    out = {
+        "metric": METRIC, "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": "attention projection: x bf16 [4096 tokens, 4096] ~N(0,1) with 41 "
+                               "outlier channels x50, W bf16 [4096, 4096] ~N(0,0.02), block 128; "
+                               "fused forward, weight pre-quantized",
+                   "M": M, "K": K, "N": N, "block": 128},
+        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def gemm_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if it
+    was taken on the current GEMM source; else None."""
+    p = os.path.join(ROOT, "profiles", "gemm_i8_attn_4096_pmc.json")
+    src = os.path.join(ROOT, "w8a8_rotated_int8_amd", "csrc", "gemm.hip")
+    try:
+        rec = json.load(open(p))
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("gemm_source_sha256") == h:
+            return rec.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def bench_embedding(cr, torch, dev, dev_normal, time_ms, wl):
+    V, D, CH, T = wl.EMBED_V, wl.EMBED_D, wl.EMBED_CHUNK, wl.EMBED_T
+    log(f"[bench] embedding: quantize [{V},{D}] in {CH}-row chunks, lookup {T} ids")
+    E = dev_normal((V, D), wl.SIGMA_W, 5)
+    qe = torch.empty((V, D), dtype=torch.int8, device=dev)
+    se = torch.empty((V,), dtype=torch.float32, device=dev)
+    q_ms = time_ms(lambda: cr.quantize_weight(E, chunk_rows=CH, out=(qe, se)), 2, 10)
+    q_bytes = V * D * 3 + 4 * V
+    del E
+    ids = torch.from_numpy(wl.embed_ids(0)).to(dev)
+    out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    l_ms = time_ms(lambda: cr.embedding_lookup(ids, qe, se, out=out), 5, 50)
+    l_bytes = T * (4 + D + 4 + 2 * D)
+    r = {
+        "embed_quant_us": round(q_ms * 1e3, 1),
+        "embed_quant_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+        "embed_quant_pct_hbm": round(100 * q_bytes / (q_ms * 1e-3) / 1e9 / 8000.0, 1),
+        "embed_lookup_us": round(l_ms * 1e3, 1),
+        "embed_lookup_GBps": round(l_bytes / (l_ms * 1e-3) / 1e9, 1),
+        "embed_lookup_pct_hbm": round(100 * l_bytes / (l_ms * 1e-3) / 1e9 / 8000.0, 1),
+    }
+    log(f"[bench] embedding quant {r['embed_quant_us']} us ({r['embed_quant_GBps']} GB/s), lookup "
+        f"{r['embed_lookup_us']} us ({r['embed_lookup_GBps']} GB/s)")
+    return r
+
+
+def bench_mlp(cr, torch, dev, dev_normal, time_ms, wl):
+    import numpy as np
+    M, D, F = 4096, 4096, 16384
+    log("[bench] MLP pair: up [16384,4096], down [4096,16384], fwd + both dX modes")
+    cols = wl.outlier_columns(D, wl.n_outliers(D), 0)
+    x = dev_normal((M, D), 1.0, 11, cols)
+    wu = dev_normal((F, D), wl.SIGMA_W, 12)
+    wd = dev_normal((D, F), wl.SIGMA_W, 13)
+    qu, su = cr.quantize_weight(wu)
+    qd, sd = cr.quantize_weight(wd)
+    del wu, wd
+    yu = cr.linear_fwd(x, qu, su)
+    h = torch.nn.functional.gelu(yu.float()).to(torch.bfloat16)
+    dyd = dev_normal((M, D), wl.SIGMA_DY, 14)
+    dyu = dev_normal((M, F), wl.SIGMA_DY, 15)
+    ops = 2.0 * M * D * F
+    r = {}
+    ws_u = torch.empty(cr.workspace_bytes(cr.OP_LINEAR_FWD, M, F, D), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(cr.workspace_bytes(cr.OP_LINEAR_FWD, M, D, F), dtype=torch.uint8, device=dev)
+    yd = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    t = time_ms(lambda: cr.linear_fwd(x, qu, su, out=yu, workspace=ws_u), 5, 30)
+    r["mlp_up_fwd_tops"] = round(ops / (t * 1e-3) / 1e12, 1)
+    t = time_ms(lambda: cr.linear_fwd(h, qd, sd, out=yd, workspace=ws_d), 5, 30)
+    r["mlp_down_fwd_tops"] = round(ops / (t * 1e-3) / 1e12, 1)
+    dxd = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+    dxu = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    for mode, name in ((cr.BWD_INT8, "int8"), (cr.BWD_BF16, "bf16")):
+        wsd = torch.empty(cr.workspace_bytes(cr.OP_LINEAR_BWD_DX, M, D, F, mode), dtype=torch.uint8, device=dev)
+        wsu = torch.empty(cr.workspace_bytes(cr.OP_LINEAR_BWD_DX, M, F, D, mode), dtype=torch.uint8, device=dev)
+        t = time_ms(lambda: cr.linear_bwd_dx(dyd, qd, sd, mode, out=dxd, workspace=wsd), 3, 20)
+        r[f"mlp_down_dx_{name}_tops"] = round(ops / (t * 1e-3) / 1e12, 1)
+        t = time_ms(lambda: cr.linear_bwd_dx(dyu, qu, su, mode, out=dxu, workspace=wsu), 3, 20)
+        r[f"mlp_up_dx_{name}_tops"] = round(ops / (t * 1e-3) / 1e12, 1)
+        del wsd, wsu
+    log(f"[bench] MLP {r}")
+    return r
+
+
+def bench_packed(cr, torch, dev, dev_normal, time_ms, wl):
+    T, K, N, L = 20480, 4096, 4096, 252
+    log(f"[bench] packed stream: {L} linears [{N},{K}] on {T} packed tokens, fwd + int8 dX")
+    cols = wl.outlier_columns(K, wl.n_outliers(K), 0)
+    x = dev_normal((T, K), 1.0, 21, cols)
+    dy = dev_normal((T, N), wl.SIGMA_DY, 22)
+    qws, sws = [], []
+    qt_ms = 0.0
+    for layer in range(L):
+        w = dev_normal((N, K), wl.SIGMA_W, 1000 + layer)
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        q, sc = cr.quantize_weight(w)
+        e.record()
+        e.synchronize()
+        qt_ms += s.elapsed_time(e)
+        qws.append(q)
+        sws.append(sc)
+        del w
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+    wsf = torch.empty(cr.workspace_bytes(cr.OP_LINEAR_FWD, T, N, K), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(cr.workspace_bytes(cr.OP_LINEAR_BWD_DX, T, N, K, cr.BWD_INT8), dtype=torch.uint8, device=dev)
+
+    def stream_pass():
+        for i in range(L):
+            cr.linear_fwd(x, qws[i], sws[i], out=y, workspace=wsf)
+            cr.linear_bwd_dx(dy, qws[i], sws[i], cr.BWD_INT8, out=dx, workspace=wsb)
+
+    t = time_ms(stream_pass, 1, 3)
+    ops = 2 * 2.0 * T * N * K * L
+    r = {
+        "packed_fwd_dx_int8_ms_per_pass": round(t, 2),
+        "packed_tokens_per_s": round(T / (t * 1e-3), 0),
+        "packed_tops": round(ops / (t * 1e-3) / 1e12, 1),
+        "packed_weight_quant_ms_total": round(qt_ms, 2),
+    }
+    log(f"[bench] packed {r}")
+    return r
+
+
+def cpu_baseline(a):
+    import numpy as np
+
+    import oracle
+    log("[bench] CPU oracle on the full attention-projection forward")
+    oq, os_, _ = oracle.rotate_quantize(a["w"])   # load time, not timed
+    t0 = time.perf_counter()
+    oracle.linear_fwd(a["x"], oq, os_)
+    dt = time.perf_counter() - t0
+    ops = 2.0 * a["M"] * a["N"] * a["K"]
+    r = {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": oracle.num_threads(),
+         "kind": "oracle", "seconds": round(dt, 2),
+         "sample": "full attention-projection forward (M=K=N=4096: rotate+quantize x, int32 "
+                   "triple-loop GEMM, fp64 epilogue), weight quantized beforehand"}
+    log(f"[bench] CPU oracle {dt:.1f} s -> {r['value']} TOPS on {r['cores']} threads")
+    return r
+
+
+if __name__ == "__main__":
+    main()

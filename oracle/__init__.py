@@ -51,6 +51,8 @@ def lib():
         L.oracle_double_to_bf16.restype = C.c_uint16
         L.oracle_rne_integer.argtypes = [C.c_double]
         L.oracle_rne_integer.restype = C.c_double
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = C.c_int
         for name in ("oracle_hadamard", "oracle_rotate_rows", "oracle_quantize_rows",
                      "oracle_rotate_quantize", "oracle_gemm_i8_i32", "oracle_dequant_epilogue",
                      "oracle_bwd_quant_dy", "oracle_gemm_i8_i32_rows_of_b",
@@ -275,6 +277,11 @@ def embedding_lookup(ids, qe, se, block: int = BLOCK):
 # --------------------------------------------------------------------------
 # Rounding helpers (pinned by the oracle's own tests)
 # --------------------------------------------------------------------------
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(lib().oracle_num_threads())
+
 
 def double_to_bf16(x: float) -> int:
     return int(lib().oracle_double_to_bf16(float(x)))

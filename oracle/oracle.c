@@ -40,6 +40,7 @@
  * so every expression below rounds exactly as written.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -442,6 +443,9 @@ int oracle_embedding_lookup(const int32_t* ids, int64_t T, const int8_t* qe, con
     if (oob) *oob = bad;
     return ORACLE_OK;
 }
+
+/* Threads the OpenMP loops above use (reported with oracle timings). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* Rounding helpers exported for the oracle's own pins. */
 uint16_t oracle_double_to_bf16(double x) { return double_to_bf16(x); }
