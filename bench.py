@@ -128,7 +128,7 @@ def main():
     ms_step = ev0.elapsed_time(ev1) / args.steps
     tops = ops / (ms_step * 1e-3) / 1e12
     log(f"[bench] linear_fwd {ms_step * 1e3:.1f} us/call  {tops:.1f} TOPS  "
-        f"({100 * tops / PEAK_INT8_TOPS:.1f}% of int8 peak; host wall {wall * 1e3 / args.steps:.1f} us)")
+        f"({100 * tops / PEAK_INT8_TOPS:.1f}% of int8 peak; host wall {wall * 1e6 / args.steps:.1f} us)")
 
     # dominant kernel alone: int8 GEMM + dequantizing epilogue
     qx, sx = cr.quantize_act(x)

@@ -25,8 +25,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
 }
+// Two fp32 -> packed bf16 pair with the hardware conversion (round to nearest
+// even, v_cvt_pk_bf16_f32).
+typedef __bf16 convrot_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float convrot_f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  convrot_f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, convrot_bf16x2));
 }
 
 // Correctly rounded fp32 quotient r / s for a per-row divisor s with a

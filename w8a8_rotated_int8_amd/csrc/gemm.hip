@@ -14,16 +14,38 @@
 //   raw int32:       test and timing hook
 //   bf16 grad_x:     bf16 operands, fp32 accumulation
 //
-// Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2, each wave
-// 128 x 128 = 4 x 4 MFMA 32x32 tiles), 128 contraction bytes per stage, two
-// LDS stages (128 KB).  Row-major operands are staged with direct 16-byte
-// global->LDS loads; each 128-byte LDS row is XOR-swizzled by
-// (row ^ row >> 3) & 7 so that both the MFMA fragment reads (32 consecutive
-// rows) and the transposed writes (rows 8 apart) are bank-conflict free.  The
-// MFMA "A" operand is P, so each lane ends with 4 consecutive i for one j:
-// the epilogue writes 8-byte (bf16) or 16-byte (int32) pieces of an output row.
+// Tiling: a 256 x 256 output tile per workgroup.  WI x WJ waves split it into
+// wave tiles of (256/WI) x (256/WJ), each a grid of 32x32 MFMA tiles.  The
+// contraction advances BK bytes per stage through a ring of STAGES LDS
+// buffers; loads run STAGES-1 stages ahead of the MFMAs.  Row-major operands
+// are staged with direct 16-byte global->LDS loads.  LDS rows (BK bytes) are
+// XOR-swizzled at 16-byte granularity so that the MFMA fragment reads (32
+// consecutive rows, one 16-byte chunk each) hit distinct banks.  P is the MFMA
+// "A" operand, so each lane ends with 4 consecutive i for one j: the epilogue
+// writes 8-byte (bf16) or 16-byte (int32) pieces of an output row.
+//
+// Workgroups are mapped to tiles XCD-aware: the hardware deals workgroups to
+// the 8 XCDs round-robin, so consecutive dispatch ids are first regrouped per
+// XCD, and each XCD then walks a compact block of tiles (GROUP_J j-tiles wide)
+// whose P and Q rows are shared through that XCD's L2.
 #include "common.h"
 #include "kernels.h"
+
+#ifndef CONVROT_GEMM_WI
+#define CONVROT_GEMM_WI 2
+#endif
+#ifndef CONVROT_GEMM_WJ
+#define CONVROT_GEMM_WJ 4
+#endif
+#ifndef CONVROT_GEMM_BK
+#define CONVROT_GEMM_BK 128
+#endif
+#ifndef CONVROT_GEMM_STAGES
+#define CONVROT_GEMM_STAGES 2
+#endif
+#ifndef CONVROT_GEMM_GROUP_J
+#define CONVROT_GEMM_GROUP_J 4
+#endif
 
 namespace convrot {
 namespace {
@@ -34,13 +56,17 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kTile = 256;
-constexpr int kBK = 128;                       // contraction bytes per stage
-constexpr int kStage = kTile * kBK;            // bytes per operand per stage
-constexpr int kLdsBytes = 4 * kStage;          // 2 stages x (P, Q)
+constexpr int kNumXcd = 8;
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// 16-byte chunk swizzle of an LDS row of BK bytes.
+template <int BK>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (BK == 128) return (row ^ (row >> 3)) & 7;
+  else return (row >> 1) & 3;
+}
+template <int BK>
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * kBK + 16 * (chunk ^ swz(row));
+  return row * BK + 16 * (chunk ^ swz<BK>(row));
 }
 
 template <bool BF16>
@@ -63,20 +89,67 @@ __device__ __forceinline__ v16f mfma(uint4 a, uint4 b, v16f c) {
                                                 __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
-// Stage rows [row0, row0 + 256) x bytes [kb0, kb0 + 128) of a row-major operand.
-// Rows past the end are clamped to the last row (their results are discarded).
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left alone (gfx9 encoding: vmcnt
+// bits [3:0] and [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | (((N >> 4) & 3) << 14));
+  asm volatile("" ::: "memory");
+}
+// Wait until at most `later` stages of LOADS direct-to-LDS loads each are in flight.
+template <int LOADS, int MAXLATER>
+__device__ __forceinline__ void wait_stages(int later) {
+  if constexpr (MAXLATER >= 4) { if (later >= 4) { wait_vm<LOADS * 4>(); return; } }
+  if constexpr (MAXLATER >= 3) { if (later >= 3) { wait_vm<LOADS * 3>(); return; } }
+  if constexpr (MAXLATER >= 2) { if (later >= 2) { wait_vm<LOADS * 2>(); return; } }
+  if constexpr (MAXLATER >= 1) { if (later >= 1) { wait_vm<LOADS>(); return; } }
+  wait_vm<0>();
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
+// would wait for every outstanding load, including the prefetched stages.
+// Callers wait explicitly for the data they need before it.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("s_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16-byte direct global->LDS load (lane i's bytes land at lds_base + 16 i).
+// Issued through inline asm so that the compiler does not fence every later
+// LDS read on it; the kernel orders the data with explicit vmcnt waits and
+// barriers instead.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// Stage rows [row0, row0 + 256) x bytes [kb0, kb0 + BK) of a row-major operand
+// into an LDS buffer of 256 rows x BK bytes.  Rows past the end are clamped to
+// the last row (their results are discarded).  NT threads; each DMA
+// instruction fills 1 KB of LDS.
+template <int BK, int NT>
 __device__ __forceinline__ void stage_rows(const uint8_t* base, int64_t ld_bytes, int64_t row0,
                                            int64_t nrows, int64_t kb0, uint8_t* lds_stage,
-                                           int wave, int lane) {
+                                           int tid) {
+  constexpr int kChunks = BK / 16;
+  constexpr int kIters = kTile * kChunks / NT;
+  const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int blk = i * 4 + wave;            // 1 KB block of the stage = 8 rows
-    int slot = blk * 64 + lane;
-    int row = slot >> 3;
-    int chunk = (slot & 7) ^ swz(row);
+  for (int it = 0; it < kIters; ++it) {
+    const int blk = it * (NT / 64) + wave;  // 1 KB block of the stage
+    const int slot = blk * 64 + lane;
+    const int row = slot / kChunks;
+    const int chunk = (slot % kChunks) ^ swz<BK>(row);
     int64_t gr = row0 + row;
     gr = gr < nrows ? gr : nrows - 1;
-    load_lds_16(base + gr * ld_bytes + kb0 + 16 * chunk, lds_stage + blk * 1024);
+    dma16(base + gr * ld_bytes + kb0 + 16 * chunk,
+          __builtin_amdgcn_readfirstlane(lds_u32(lds_stage) + blk * 1024));
   }
 }
 
@@ -94,17 +167,18 @@ __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c,
   o3 = __builtin_amdgcn_perm(u1, t1, 0x07060302u);         // a3 b3 c3 d3
 }
 
-// Transposed int8 operand: source [Kc, I] (I contiguous).  Each lane loads a
-// 16 (k) x 8 (i) byte block with 8-byte loads (32 lanes cover the 256 i of the
-// tile in one row), transposes it in registers and writes 8 LDS rows (one per
-// i) of 16 k-bytes each.
+// Transposed int8 operand (BK = 128, 256 threads): source [Kc, I] (I
+// contiguous).  Each lane loads a 16 (k) x 8 (i) byte block with 8-byte loads
+// (32 lanes cover the 256 i of the tile in one row), transposes it in
+// registers and writes 8 LDS rows (one per i) of 16 k-bytes each.
 struct TransposedRegs {
   uint2 r[16];
 };
 
 __device__ __forceinline__ void load_transposed(const int8_t* src, int64_t ld, int64_t I,
-                                                int64_t i0, int64_t k0, int wave, int lane,
+                                                int64_t i0, int64_t k0, int tid,
                                                 TransposedRegs& t) {
+  const int lane = tid & 63, wave = tid >> 6;
   int ic = lane & 31;
   int kg = (lane >> 5) + 2 * wave;
   int64_t i = i0 + 8 * ic;
@@ -115,7 +189,8 @@ __device__ __forceinline__ void load_transposed(const int8_t* src, int64_t ld, i
 }
 
 __device__ __forceinline__ void store_transposed(const TransposedRegs& t, uint8_t* lds_stage,
-                                                 int wave, int lane) {
+                                                 int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
   int ic = lane & 31;
   int kg = (lane >> 5) + 2 * wave;
   uint32_t o[8][4];  // o[j][d]: bytes (k = 4d .. 4d+3) of column i = 8 ic + j
@@ -128,214 +203,306 @@ __device__ __forceinline__ void store_transposed(const TransposedRegs& t, uint8_
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    *reinterpret_cast<uint4*>(lds_stage + lds_off(8 * ic + j, kg)) =
+    *reinterpret_cast<uint4*>(lds_stage + lds_off<128>(8 * ic + j, kg)) =
         make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]);
   }
 }
 
-template <int EPI, bool PT, bool BF16>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
+// Dispatch id -> (i tile, j tile), XCD-aware (see the file comment).
+__device__ __forceinline__ void tile_of(int64_t gi, int64_t gj, int& ti, int& tj) {
+  const int64_t nb = gi * gj;
+  int64_t b = blockIdx.x;
+  if (nb % kNumXcd == 0) b = (b % kNumXcd) * (nb / kNumXcd) + b / kNumXcd;
+  const int64_t G = CONVROT_GEMM_GROUP_J;
+  const int64_t per_group = G * gi;
+  const int64_t group = b / per_group;
+  const int64_t first_j = group * G;
+  const int64_t gsize = gj - first_j < G ? gj - first_j : G;
+  const int64_t r = b % per_group;
+  tj = (int)(first_j + r % gsize);
+  ti = (int)(r / gsize);
+}
+
+template <int EPI, bool PT, bool BF16, int WI, int WJ, int BK, int STAGES>
+__global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   typedef typename AccT<BF16>::type acc_t;
   constexpr int esz = BF16 ? 2 : 1;
+  constexpr int NT = 64 * WI * WJ;
+  constexpr int TI = kTile / WI, TJ = kTile / WJ;  // wave tile
+  constexpr int NI = TI / 32, NJ = TJ / 32;        // MFMA tiles per wave
+  constexpr int kStage = kTile * BK;               // bytes per operand per stage
+  constexpr int kLoadsPerStage = 2 * kTile * (BK / 16) / NT;  // DMA per thread per stage
+  static_assert(!PT || (BK == 128 && NT == 256 && STAGES == 2), "transposed P: BK 128, 4 waves");
+  static_assert(EPI != kEpiInvRotBf16 || TI == 128, "inverse rotation needs 128-wide wave tiles");
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wi = wave & 1, wj = wave >> 1;
-  const int64_t i0 = (int64_t)blockIdx.x * kTile;
-  const int64_t j0 = (int64_t)blockIdx.y * kTile;
-  const int64_t kbytes = a.Kc * esz;
-  const int nk = (int)(kbytes / kBK);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wi = wave % WI, wj = wave / WI;
+  const int64_t gi = (a.I + kTile - 1) / kTile, gj = (a.J + kTile - 1) / kTile;
+  int ti, tj;
+  tile_of(gi, gj, ti, tj);
+  const int64_t i0 = (int64_t)ti * kTile;
+  const int64_t j0 = (int64_t)tj * kTile;
+  const int nk = (int)(a.Kc * esz / BK);
 
   const uint8_t* P = static_cast<const uint8_t*>(a.P);
   const uint8_t* Q = static_cast<const uint8_t*>(a.Q);
-
   auto Ps = [&](int buf) { return lds + buf * 2 * kStage; };
   auto Qs = [&](int buf) { return lds + buf * 2 * kStage + kStage; };
 
-  acc_t acc[4][4];
+  acc_t acc[NI][NJ];
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < NI; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = acc_t{};
+    for (int y = 0; y < NJ; ++y) acc[x][y] = acc_t{};
 
-  TransposedRegs tr;
-  // prologue: stage 0
-  stage_rows(Q, a.ldq * esz, j0, a.J, 0, Qs(0), wave, lane);
-  if (PT) {
-    load_transposed(static_cast<const int8_t*>(a.P), a.ldp, a.I, i0, 0, wave, lane, tr);
-    store_transposed(tr, Ps(0), wave, lane);
-  } else {
-    stage_rows(P, a.ldp * esz, i0, a.I, 0, Ps(0), wave, lane);
-  }
+  auto issue_stage = [&](int kt, int buf) {
+    const int64_t kb = (int64_t)kt * BK;
+    stage_rows<BK, NT>(P, a.ldp * esz, i0, a.I, kb, Ps(buf), tid);
+    stage_rows<BK, NT>(Q, a.ldq * esz, j0, a.J, kb, Qs(buf), tid);
+  };
 
-  int buf = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vmem();
-    __syncthreads();
-    const bool more = kt + 1 < nk;
-    if (more) {
-      int64_t kb = (int64_t)(kt + 1) * kBK;
-      stage_rows(Q, a.ldq * esz, j0, a.J, kb, Qs(buf ^ 1), wave, lane);
-      if (PT) {
-        load_transposed(static_cast<const int8_t*>(a.P), a.ldp, a.I, i0, kb, wave, lane, tr);
-      } else {
-        stage_rows(P, a.ldp * esz, i0, a.I, kb, Ps(buf ^ 1), wave, lane);
-      }
-    }
+  auto compute_stage = [&](int buf) {
     const uint8_t* ps = Ps(buf);
     const uint8_t* qs = Qs(buf);
 #pragma unroll
-    for (int s = 0; s < kBK / 32; ++s) {
-      uint4 pf[4], qf[4];
+    for (int s = 0; s < BK / 32; ++s) {
+      uint4 pf[NI], qf[NJ];
       const int chunk = 2 * s + (lane >> 5);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        pf[t] = *reinterpret_cast<const uint4*>(ps + lds_off(wi * 128 + t * 32 + (lane & 31), chunk));
-        qf[t] = *reinterpret_cast<const uint4*>(qs + lds_off(wj * 128 + t * 32 + (lane & 31), chunk));
-      }
+      for (int t = 0; t < NI; ++t)
+        pf[t] = *reinterpret_cast<const uint4*>(ps + lds_off<BK>(wi * TI + t * 32 + (lane & 31), chunk));
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int t = 0; t < NJ; ++t)
+        qf[t] = *reinterpret_cast<const uint4*>(qs + lds_off<BK>(wj * TJ + t * 32 + (lane & 31), chunk));
 #pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = mfma(pf[x], qf[y], acc[x][y]);
+      for (int x = 0; x < NI; ++x)
+#pragma unroll
+        for (int y = 0; y < NJ; ++y) acc[x][y] = mfma(pf[x], qf[y], acc[x][y]);
     }
-    if (PT && more) store_transposed(tr, Ps(buf ^ 1), wave, lane);
-    buf ^= 1;
+  };
+
+  if constexpr (PT) {
+    TransposedRegs tr;
+    stage_rows<BK, NT>(Q, a.ldq * esz, j0, a.J, 0, Qs(0), tid);
+    load_transposed(static_cast<const int8_t*>(a.P), a.ldp, a.I, i0, 0, tid, tr);
+    store_transposed(tr, Ps(0), tid);
+    int buf = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vm<0>();
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+      raw_barrier();
+      const bool more = kt + 1 < nk;
+      if (more) {
+        const int64_t kb = (int64_t)(kt + 1) * BK;
+        load_transposed(static_cast<const int8_t*>(a.P), a.ldp, a.I, i0, kb, tid, tr);
+        stage_rows<BK, NT>(Q, a.ldq * esz, j0, a.J, kb, Qs(buf ^ 1), tid);
+      }
+      compute_stage(buf);
+      if (more) store_transposed(tr, Ps(buf ^ 1), tid);
+      buf ^= 1;
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) issue_stage(s, s);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int later = nk - 1 - kt < STAGES - 2 ? nk - 1 - kt : STAGES - 2;
+      wait_stages<kLoadsPerStage, STAGES - 2>(later);
+      raw_barrier();
+      if (kt + STAGES - 1 < nk) issue_stage(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+      compute_stage(kt % STAGES);
+    }
   }
 
   // ---- epilogue -------------------------------------------------------------
   const int h = lane >> 5;
-  if (EPI == kEpiInvRotBf16) {
-    const int64_t iblk = i0 + wi * 128;
-    if (iblk >= a.I) return;
-    uint16_t* out = static_cast<uint16_t*>(a.out);
+  if constexpr (EPI == kEpiI32) {
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int64_t j = j0 + wj * 128 + y * 32 + (lane & 31);
-      const float sjv = j < a.J ? a.sj[j] : 0.f;
-      float w[64];
+    for (int y = 0; y < NJ; ++y) {
+      const int64_t j = j0 + wj * TJ + y * 32 + (lane & 31);
+      if (j >= a.J) continue;
+      int32_t* orow = static_cast<int32_t*>(a.out) + j * a.ldo;
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int x = 0; x < NI; ++x) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) w[x * 16 + r] = (float)acc[x][y][r] * sjv;
-#pragma unroll
-      for (int bit = 1; bit < 64; bit <<= 1) {
-#pragma unroll
-        for (int e = 0; e < 64; ++e) {
-          if (e & bit) continue;
-          float u = w[e], v = w[e | bit];
-          w[e] = u + v;
-          w[e | bit] = u - v;
+        for (int g = 0; g < 4; ++g) {
+          const int64_t i = i0 + wi * TI + x * 32 + 8 * g + 4 * h;
+          if (i >= a.I) continue;
+          int vv[4] = {(int)acc[x][y][4 * g], (int)acc[x][y][4 * g + 1],
+                       (int)acc[x][y][4 * g + 2], (int)acc[x][y][4 * g + 3]};
+          if (i + 4 <= a.I) {
+            *reinterpret_cast<int4*>(orow + i) = make_int4(vv[0], vv[1], vv[2], vv[3]);
+          } else {
+            for (int u = 0; u < 4 && i + u < a.I; ++u) orow[i + u] = vv[u];
+          }
         }
       }
+    }
+  } else {
+    // bf16 results: each wave stages its TJ x TI sub-tile in LDS (rows of TI
+    // bf16, 16-byte chunks XOR-swizzled by the row), then writes 16-byte
+    // pieces of contiguous output rows, so every store instruction covers whole
+    // cache lines instead of 16 bytes of 32 different rows.
+    constexpr int kRowBytes = TI * 2;
+    constexpr int kChunkMask = TI / 8 - 1;
+    static_assert(WI * WJ * TJ * kRowBytes <= STAGES * 2 * kStage, "staging fits the LDS ring");
+    raw_barrier();  // all waves are done with the operand ring
+    uint8_t* stg = lds + wave * TJ * kRowBytes;
+    auto put8 = [&](int jl, int il, uint32_t lo, uint32_t hi) {
+      const int pos = (il >> 3) ^ (jl & kChunkMask);
+      *reinterpret_cast<uint2*>(stg + jl * kRowBytes + pos * 16 + (il & 7) * 2) = make_uint2(lo, hi);
+    };
+    if constexpr (EPI == kEpiInvRotBf16) {
+      static_assert(TI == 128, "one wave owns whole 128-blocks along i");
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        swap_halves(w[e], w[e + 32]);
-        float u = w[e], v = w[e + 32];
-        w[e] = u + v;
-        w[e + 32] = u - v;
-      }
-      if (j < a.J) {
+      for (int y = 0; y < NJ; ++y) {
+        const int jl = y * 32 + (lane & 31);
+        const int64_t j = j0 + wj * TJ + jl;
+        const float sjv = j < a.J ? a.sj[j] : 0.f;
+        float w[64];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) w[x * 16 + r] = (float)acc[x][y][r] * sjv;
+        // w index bits 0-1 -> i bits 0-1, bits 2-3 -> i bits 3-4, bits 4-5 ->
+        // i bits 5-6; the lane half h is i bit 2.
+#pragma unroll
+        for (int bit = 1; bit < 64; bit <<= 1) {
+#pragma unroll
+          for (int e = 0; e < 64; ++e) {
+            if (e & bit) continue;
+            float u = w[e], v = w[e | bit];
+            w[e] = u + v;
+            w[e | bit] = u - v;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          swap_halves(w[e], w[e + 32]);
+          float u = w[e], v = w[e + 32];
+          w[e] = u + v;
+          w[e + 32] = u - v;
+        }
         const float cf = (float)kInvSqrt128;
-        uint16_t* orow = out + j * a.ldo + iblk;
 #pragma unroll
         for (int q4 = 0; q4 < 8; ++q4) {
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
             const int e = 4 * q4 + 32 * half;
             const int il = ((q4 & 3) << 3) | ((q4 >> 2) << 5) | (h << 6) | (half << 2);
-            uint2 pk = make_uint2(pack_bf16x2(w[e] * cf, w[e + 1] * cf),
-                                  pack_bf16x2(w[e + 2] * cf, w[e + 3] * cf));
-            *reinterpret_cast<uint2*>(orow + il) = pk;
+            put8(jl, il, pack_bf16x2(w[e] * cf, w[e + 1] * cf),
+                 pack_bf16x2(w[e + 2] * cf, w[e + 3] * cf));
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int y = 0; y < NJ; ++y) {
+        const int jl = y * 32 + (lane & 31);
+        const int64_t j = j0 + wj * TJ + jl;
+        float sjv = 1.f;
+        if constexpr (EPI == kEpiDequantBf16) sjv = j < a.J ? a.sj[j] : 0.f;
+#pragma unroll
+        for (int x = 0; x < NI; ++x) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int il = x * 32 + 8 * g + 4 * h;
+            const int64_t i = i0 + wi * TI + il;
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = (float)acc[x][y][4 * g + u];
+            if constexpr (EPI == kEpiDequantBf16) {
+              if (i + 4 <= a.I) {
+                const float4 s4 = *reinterpret_cast<const float4*>(a.si + i);
+                v[0] = v[0] * sjv * s4.x;
+                v[1] = v[1] * sjv * s4.y;
+                v[2] = v[2] * sjv * s4.z;
+                v[3] = v[3] * sjv * s4.w;
+              } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                  const int64_t iu = i + u < a.I ? i + u : a.I - 1;
+                  v[u] = v[u] * sjv * a.si[iu];
+                }
+              }
+              if (a.bias) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                  const int64_t iu = i + u < a.I ? i + u : a.I - 1;
+                  v[u] = v[u] + __uint_as_float((uint32_t)a.bias[iu] << 16);
+                }
+              }
+            }
+            put8(jl, il, pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
           }
         }
       }
     }
-    return;
-  }
-
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes landed
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    // read back: TJ rows x (TI / 8) chunks of 16 bytes, 64 lanes per step
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+    constexpr int kChunks = TJ * (TI / 8);
 #pragma unroll
-  for (int y = 0; y < 4; ++y) {
-    const int64_t j = j0 + wj * 128 + y * 32 + (lane & 31);
-    if (j >= a.J) continue;
-    float sjv = 1.f;
-    if (EPI == kEpiDequantBf16) sjv = a.sj[j];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t i = i0 + wi * 128 + x * 32 + 8 * g + 4 * h;
-        if (i >= a.I) continue;
-        const bool full = i + 4 <= a.I;
-        if (EPI == kEpiI32) {
-          int32_t* orow = static_cast<int32_t*>(a.out) + j * a.ldo;
-          int v0 = (int)acc[x][y][4 * g], v1 = (int)acc[x][y][4 * g + 1],
-              v2 = (int)acc[x][y][4 * g + 2], v3 = (int)acc[x][y][4 * g + 3];
-          if (full) {
-            *reinterpret_cast<int4*>(orow + i) = make_int4(v0, v1, v2, v3);
-          } else {
-            int vv[4] = {v0, v1, v2, v3};
-            for (int u = 0; u < 4 && i + u < a.I; ++u) orow[i + u] = vv[u];
-          }
-        } else {
-          float v[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] = (float)acc[x][y][4 * g + u];
-          if (EPI == kEpiDequantBf16) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              int64_t iu = i + u < a.I ? i + u : a.I - 1;
-              float sv = a.si[iu];
-              float t = v[u] * sjv * sv;
-              if (a.bias) t = t + bf16lo_to_f32(a.bias[iu]);
-              v[u] = t;
-            }
-          }
-          uint16_t* orow = static_cast<uint16_t*>(a.out) + j * a.ldo;
-          if (full) {
-            *reinterpret_cast<uint2*>(orow + i) =
-                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-          } else {
-            for (int u = 0; u < 4 && i + u < a.I; ++u) orow[i + u] = (uint16_t)f32_to_bf16_rne(v[u]);
-          }
-        }
+    for (int c0 = 0; c0 < kChunks; c0 += 64) {
+      const int idx = c0 + lane;
+      const int jl = idx / (TI / 8), c = idx % (TI / 8);
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + jl * kRowBytes + ((c ^ (jl & kChunkMask)) * 16));
+      const int64_t j = j0 + wj * TJ + jl;
+      const int64_t i = i0 + wi * TI + 8 * c;
+      if (j >= a.J || i >= a.I) continue;
+      uint16_t* dst = out + j * a.ldo + i;
+      if (i + 8 <= a.I) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else {
+        const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+        for (int u = 0; u < 8 && i + u < a.I; ++u) dst[u] = (uint16_t)(wds[u >> 1] >> (16 * (u & 1)));
       }
     }
   }
 }
 
-template <int EPI, bool PT, bool BF16>
+template <int EPI, bool PT, bool BF16, int WI, int WJ, int BK, int STAGES>
 hipError_t launch(const GemmArgs& a, hipStream_t stream) {
+  constexpr int kLds = STAGES * 2 * kTile * BK;
+  auto kern = gemm_kernel<EPI, PT, BF16, WI, WJ, BK, STAGES>;
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<EPI, PT, BF16>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  int64_t gi = (a.I + kTile - 1) / kTile, gj = (a.J + kTile - 1) / kTile;
+  const int64_t gi = (a.I + kTile - 1) / kTile, gj = (a.J + kTile - 1) / kTile;
   if (gi <= 0 || gj <= 0) return hipSuccess;
-  if (gi > 0x7fffffff || gj > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_kernel<EPI, PT, BF16>), dim3((unsigned)gi, (unsigned)gj), dim3(256),
-                     kLdsBytes, stream, a);
+  if (gi * gj > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(gi * gj)), dim3(64 * WI * WJ), kLds, stream, a);
   return hipGetLastError();
 }
+
+constexpr int kWI = CONVROT_GEMM_WI, kWJ = CONVROT_GEMM_WJ;
+constexpr int kBK = CONVROT_GEMM_BK, kStages = CONVROT_GEMM_STAGES;
 
 }  // namespace
 
 hipError_t launch_gemm_i8(const GemmArgs& a, int epilogue, bool p_transposed, hipStream_t stream) {
   if (p_transposed) {
-    if (epilogue == kEpiI32) return launch<kEpiI32, true, false>(a, stream);
-    if (epilogue == kEpiInvRotBf16) return launch<kEpiInvRotBf16, true, false>(a, stream);
+    if (epilogue == kEpiI32) return launch<kEpiI32, true, false, 2, 2, 128, 2>(a, stream);
+    if (epilogue == kEpiInvRotBf16) return launch<kEpiInvRotBf16, true, false, 2, 2, 128, 2>(a, stream);
     return hipErrorInvalidValue;
   }
-  if (epilogue == kEpiI32) return launch<kEpiI32, false, false>(a, stream);
-  if (epilogue == kEpiDequantBf16) return launch<kEpiDequantBf16, false, false>(a, stream);
+  if (epilogue == kEpiI32) return launch<kEpiI32, false, false, kWI, kWJ, kBK, kStages>(a, stream);
+  if (epilogue == kEpiDequantBf16)
+    return launch<kEpiDequantBf16, false, false, kWI, kWJ, kBK, kStages>(a, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t stream) {
-  return launch<kEpiBf16, false, true>(a, stream);
+  return launch<kEpiBf16, false, true, kWI, kWJ, kBK, kStages>(a, stream);
 }
 
 }  // namespace convrot
