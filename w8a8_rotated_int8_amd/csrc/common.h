@@ -99,6 +99,31 @@ __device__ __forceinline__ void wait_vmem() {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// 32-bit LDS address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left alone (gfx9 encoding: vmcnt
+// bits [3:0] and [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | (((N >> 4) & 3) << 14));
+  asm volatile("" ::: "memory");
+}
+
+// 16-byte direct global->LDS load (lane i's bytes land at lds_base + 16 i;
+// lds_base must be wave-uniform).  Issued through inline asm so that the
+// compiler does not fence every later LDS access on it: callers order the
+// data with explicit vmcnt waits (and barriers when other waves read it).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+
 // 16-byte direct global->LDS load: lane i's 16 bytes land at lds_base + 16*i.
 __device__ __forceinline__ void load_lds_16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);

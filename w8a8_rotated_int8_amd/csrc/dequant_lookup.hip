@@ -55,61 +55,132 @@ __device__ __forceinline__ void fwht_codes(const uint4 raw[4], float w[64]) {
 // LDS position (16-byte units) of chunk c (0..7) of int8 block b.
 __device__ __forceinline__ int lds_chunk8(int b, int c) { return (b << 3) | (c ^ (b & 7)); }
 
+// Store the 64 outputs of this lane's half block (see fwht_codes) scaled by rs.
+__device__ __forceinline__ void store_block_half(uint16_t* blk_out, int h, const float w[64],
+                                                 float rs) {
+  uint4* d0 = reinterpret_cast<uint4*>(blk_out + 32 * h);
+  uint4* d1 = reinterpret_cast<uint4*>(blk_out + 64 + 32 * h);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    d0[g] = make_uint4(pack_bf16x2(w[8 * g] * rs, w[8 * g + 1] * rs),
+                       pack_bf16x2(w[8 * g + 2] * rs, w[8 * g + 3] * rs),
+                       pack_bf16x2(w[8 * g + 4] * rs, w[8 * g + 5] * rs),
+                       pack_bf16x2(w[8 * g + 6] * rs, w[8 * g + 7] * rs));
+    d1[g] = make_uint4(pack_bf16x2(w[32 + 8 * g] * rs, w[32 + 8 * g + 1] * rs),
+                       pack_bf16x2(w[32 + 8 * g + 2] * rs, w[32 + 8 * g + 3] * rs),
+                       pack_bf16x2(w[32 + 8 * g + 4] * rs, w[32 + 8 * g + 5] * rs),
+                       pack_bf16x2(w[32 + 8 * g + 6] * rs, w[32 + 8 * g + 7] * rs));
+  }
+}
+
+// Issue the 4 direct-to-LDS loads of a row span of span (1..32) int8 blocks;
+// slots past the span reload its last chunk so every lane issues 4 loads.
+__device__ __forceinline__ void stage_row(const int8_t* row, int span, uint8_t* buf) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_u32(buf));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int slot = i * 64 + lane;
+    int b = slot >> 3;
+    int c = (slot & 7) ^ (b & 7);
+    if (b >= span) { b = span - 1; c = 7; }
+    dma16(row + b * kBlock + 16 * c, base + i * 1024);
+  }
+}
+
+// D <= 4096: persistent waves, one token at a time; the next token's row is
+// loaded into the second LDS buffer while the current one is transformed.
+// Token ids are fetched 64 at a time into one register and broadcast with
+// readlane, so no scalar load sits between two row loads.
 __global__ __launch_bounds__(256) void embedding_lookup_kernel(
+    const int32_t* __restrict__ ids, int64_t T, const int8_t* __restrict__ qe,
+    const float* __restrict__ se, int64_t V, int D, uint16_t* __restrict__ out,
+    int32_t* __restrict__ oob) {
+  __shared__ __align__(16) uint8_t lds[4][2][4096];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = lane & 31, h = lane >> 5;
+  const int span = D / kBlock;
+  const int64_t wstride = (int64_t)gridDim.x * 4;
+  const int64_t t0 = (int64_t)blockIdx.x * 4 + wave;
+  if (t0 >= T) return;
+  const int64_t ntok = (T - 1 - t0) / wstride + 1;  // tokens of this wave
+  auto valid_id = [&](int id) { return id >= 0 && (int64_t)id < V; };
+  int id_reg = 0;
+  float sc_reg = 0.f;
+  auto load_ids = [&](int64_t k0) {  // ids and row scales of tokens k0 .. k0+63
+    const int64_t t = t0 + (k0 + lane) * wstride;
+    id_reg = (k0 + lane < ntok) ? ids[t] : 0;
+    sc_reg = valid_id(id_reg) ? se[id_reg] * (float)kInvSqrt128 : 0.f;
+  };
+  load_ids(0);
+  int id = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(id_reg, 0));
+  float rs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_reg), 0));
+  if (valid_id(id)) stage_row(qe + (int64_t)id * D, span, lds[wave][0]);
+  int cur = 0;
+  for (int64_t k = 0; k < ntok; ++k) {
+    const int64_t t = t0 + k * wstride;
+    int nid = 0;
+    float nrs = 0.f;
+    const bool more = k + 1 < ntok;
+    if (more) {
+      if (((k + 1) & 63) == 0) {
+        wait_vm_n<0>();  // the row load in flight must not pass the id load
+        load_ids(k + 1);
+      }
+      nid = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(id_reg, (int)((k + 1) & 63)));
+      nrs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_reg),
+                                                                (int)((k + 1) & 63)));
+    }
+    if (more && valid_id(nid)) {
+      stage_row(qe + (int64_t)nid * D, span, lds[wave][cur ^ 1]);
+      wait_vm_n<4>();
+    } else {
+      wait_vm_n<0>();
+    }
+    const bool valid = valid_id(id);
+    if (!valid && lane == 0 && oob) atomicAdd(oob, 1);
+    uint4 raw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      raw[i] = valid ? *reinterpret_cast<const uint4*>(lds[wave][cur] + 16 * lds_chunk8(p, 4 * h + i))
+                     : make_uint4(0, 0, 0, 0);
+    float w[64];
+    fwht_codes(raw, w);
+    if (p < span) store_block_half(out + t * (int64_t)D + (int64_t)p * kBlock, h, w, rs);
+    id = nid;
+    rs = nrs;
+    cur ^= 1;
+  }
+}
+
+// D > 4096: one token per wave, the row processed in 4096-wide spans.
+__global__ __launch_bounds__(256) void embedding_lookup_long_kernel(
     const int32_t* __restrict__ ids, int64_t T, const int8_t* __restrict__ qe,
     const float* __restrict__ se, int64_t V, int D, uint16_t* __restrict__ out,
     int32_t* __restrict__ oob) {
   __shared__ __align__(16) uint8_t lds[4][4096];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= T) return;
   const int nb = D / kBlock;
-  uint8_t* my = lds[wave];
   const int p = lane & 31, h = lane >> 5;
-
-  int64_t id = -1;
-  if (t < T) id = ids[t];
-  const bool valid = t < T && id >= 0 && id < V;
-  if (t < T && !valid && lane == 0 && oob) atomicAdd(oob, 1);
+  const int64_t id = ids[t];
+  const bool valid = id >= 0 && id < V;
+  if (!valid && lane == 0 && oob) atomicAdd(oob, 1);
   const float rs = valid ? se[id] * (float)kInvSqrt128 : 0.f;
-
   for (int b0 = 0; b0 < nb; b0 += 32) {
     const int span = nb - b0 < 32 ? nb - b0 : 32;
-    if (valid) {
-      const int8_t* row = qe + id * (int64_t)D + (int64_t)b0 * kBlock;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int slot = i * 64 + lane;
-        int b = slot >> 3;
-        int c = (slot & 7) ^ (b & 7);
-        if (b < span) load_lds_16(row + b * kBlock + 16 * c, my + i * 1024);
-      }
-    }
-    wait_vmem();
-    __builtin_amdgcn_wave_barrier();
+    if (valid) stage_row(qe + id * (int64_t)D + (int64_t)b0 * kBlock, span, lds[wave]);
+    wait_vm_n<0>();
     uint4 raw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      raw[i] = valid ? *reinterpret_cast<const uint4*>(my + 16 * lds_chunk8(p, 4 * h + i))
+      raw[i] = valid ? *reinterpret_cast<const uint4*>(lds[wave] + 16 * lds_chunk8(p, 4 * h + i))
                      : make_uint4(0, 0, 0, 0);
-    __builtin_amdgcn_wave_barrier();  // LDS reads done before the next span overwrites
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // LDS reads retired before the next span overwrites
     float w[64];
     fwht_codes(raw, w);
-    if (t < T && p < span) {
-      uint16_t* dst = out + t * (int64_t)D + (int64_t)(b0 + p) * kBlock;
-      uint4* d0 = reinterpret_cast<uint4*>(dst + 32 * h);
-      uint4* d1 = reinterpret_cast<uint4*>(dst + 64 + 32 * h);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        d0[g] = make_uint4(pack_bf16x2(w[8 * g] * rs, w[8 * g + 1] * rs),
-                           pack_bf16x2(w[8 * g + 2] * rs, w[8 * g + 3] * rs),
-                           pack_bf16x2(w[8 * g + 4] * rs, w[8 * g + 5] * rs),
-                           pack_bf16x2(w[8 * g + 6] * rs, w[8 * g + 7] * rs));
-        d1[g] = make_uint4(pack_bf16x2(w[32 + 8 * g] * rs, w[32 + 8 * g + 1] * rs),
-                           pack_bf16x2(w[32 + 8 * g + 2] * rs, w[32 + 8 * g + 3] * rs),
-                           pack_bf16x2(w[32 + 8 * g + 4] * rs, w[32 + 8 * g + 5] * rs),
-                           pack_bf16x2(w[32 + 8 * g + 6] * rs, w[32 + 8 * g + 7] * rs));
-      }
-    }
+    if (p < span) store_block_half(out + t * (int64_t)D + (int64_t)(b0 + p) * kBlock, h, w, rs);
   }
 }
 
@@ -168,10 +239,25 @@ hipError_t launch_embedding_lookup(const int32_t* ids, int64_t T, const int8_t* 
                                    const float* se, int64_t V, int64_t D, uint16_t* out,
                                    int32_t* oob, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  int64_t grid = (T + 3) / 4;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(embedding_lookup_kernel, dim3((unsigned)grid), dim3(256), 0, stream, ids, T,
-                     qe, se, V, (int)D, out, oob);
+  if (D <= 4096) {
+    static int n_cu = 0;
+    if (n_cu == 0) {
+      int dev = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess) return e;
+    }
+    int64_t grid = (T + 3) / 4;
+    const int64_t cap = 4 * (int64_t)n_cu;  // four resident workgroups per CU
+    if (grid > cap) grid = cap;
+    hipLaunchKernelGGL(embedding_lookup_kernel, dim3((unsigned)grid), dim3(256), 0, stream, ids,
+                       T, qe, se, V, (int)D, out, oob);
+  } else {
+    int64_t grid = (T + 3) / 4;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(embedding_lookup_long_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       ids, T, qe, se, V, (int)D, out, oob);
+  }
   return hipGetLastError();
 }
 

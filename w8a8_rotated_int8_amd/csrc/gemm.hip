@@ -89,14 +89,8 @@ __device__ __forceinline__ v16f mfma(uint4 a, uint4 b, v16f c) {
                                                 __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
-// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left alone (gfx9 encoding: vmcnt
-// bits [3:0] and [15:14]).
 template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | (((N >> 4) & 3) << 14));
-  asm volatile("" ::: "memory");
-}
+__device__ __forceinline__ void wait_vm() { wait_vm_n<N>(); }
 // Wait until at most `later` stages of LOADS direct-to-LDS loads each are in flight.
 template <int LOADS, int MAXLATER>
 __device__ __forceinline__ void wait_stages(int later) {
@@ -112,21 +106,6 @@ __device__ __forceinline__ void wait_stages(int later) {
 // Callers wait explicitly for the data they need before it.
 __device__ __forceinline__ void raw_barrier() {
   asm volatile("s_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// 16-byte direct global->LDS load (lane i's bytes land at lds_base + 16 i).
-// Issued through inline asm so that the compiler does not fence every later
-// LDS read on it; the kernel orders the data with explicit vmcnt waits and
-// barriers instead.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds_base)
-               : "memory", "m0");
 }
 
 // Stage rows [row0, row0 + 256) x bytes [kb0, kb0 + BK) of a row-major operand
@@ -238,7 +217,7 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wi = wave % WI, wj = wave / WI;
   const int64_t gi = (a.I + kTile - 1) / kTile, gj = (a.J + kTile - 1) / kTile;
   int ti, tj;
@@ -305,15 +284,85 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
       buf ^= 1;
     }
   } else {
+    // Per-thread source pointers and LDS destinations of the stage loads,
+    // computed once: a stage load is then one 64-bit add per instruction.
+    constexpr int kRowDma = kTile * (BK / 16) / NT;  // per operand per stage
+    const uint8_t* src[2 * kRowDma];
+    uint32_t dst_off[2 * kRowDma];
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-      if (s < nk) issue_stage(s, s);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int later = nk - 1 - kt < STAGES - 2 ? nk - 1 - kt : STAGES - 2;
-      wait_stages<kLoadsPerStage, STAGES - 2>(later);
+    for (int op = 0; op < 2; ++op) {
+#pragma unroll
+      for (int it = 0; it < kRowDma; ++it) {
+        const int blk = it * (NT / 64) + wave;
+        const int slot = blk * 64 + lane;
+        const int row = slot / (BK / 16);
+        const int chunk = (slot % (BK / 16)) ^ swz<BK>(row);
+        const int64_t row0 = op ? j0 : i0, nrows = op ? a.J : a.I;
+        int64_t gr = row0 + row;
+        gr = gr < nrows ? gr : nrows - 1;
+        src[op * kRowDma + it] = (op ? Q : P) + gr * ((op ? a.ldq : a.ldp) * esz) + 16 * chunk;
+        dst_off[op * kRowDma + it] = (op ? kStage : 0) + blk * 1024;  // uniform
+      }
+    }
+    const uint32_t lds_base = lds_u32(lds);
+    auto issue = [&](int kt, int buf) {
+      const int64_t kb = (int64_t)kt * BK;
+      const uint32_t b0 = lds_base + buf * 2 * kStage;
+#pragma unroll
+      for (int d = 0; d < 2 * kRowDma; ++d) dma16(src[d] + kb, b0 + dst_off[d]);
+    };
+    constexpr int SL = BK / 32;
+    static_assert(SL % 2 == 0, "fragment double buffer alternates per slice");
+    uint4 F[2][NI + NJ];
+    auto read_frags = [&](int buf, int s, uint4* f) {
+      const uint8_t* ps = Ps(buf);
+      const uint8_t* qs = Qs(buf);
+      const int chunk = 2 * s + (lane >> 5);
+#pragma unroll
+      for (int t = 0; t < NI; ++t)
+        f[t] = *reinterpret_cast<const uint4*>(ps + lds_off<BK>(wi * TI + t * 32 + (lane & 31), chunk));
+#pragma unroll
+      for (int t = 0; t < NJ; ++t)
+        f[NI + t] = *reinterpret_cast<const uint4*>(qs + lds_off<BK>(wj * TJ + t * 32 + (lane & 31), chunk));
+    };
+    // all STAGES buffers start filled; the buffer of stage kt is refilled with
+    // stage kt + STAGES at the end of stage kt
+#pragma unroll
+    for (int st = 0; st < STAGES; ++st)
+      if (st < nk) issue(st, st);
+    {
+      const int later = nk - 1 < STAGES - 1 ? nk - 1 : STAGES - 1;
+      wait_stages<kLoadsPerStage, STAGES - 1>(later);
       raw_barrier();
-      if (kt + STAGES - 1 < nk) issue_stage(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-      compute_stage(kt % STAGES);
+    }
+    read_frags(0, 0, F[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt % STAGES;
+#pragma unroll
+      for (int s = 0; s < SL; ++s) {
+        const bool last = s + 1 == SL;
+        if (!last) {
+          read_frags(buf, s + 1, F[(s + 1) & 1]);
+        } else if (kt + 1 < nk) {
+          // Retire this wave's reads of stage kt, wait for stage kt+1 (at most
+          // min(STAGES-2, nk-2-kt) later stages in flight) and publish; the
+          // MFMAs of earlier slices keep the matrix pipe busy meanwhile.
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+          const int later = nk - 2 - kt < STAGES - 2 ? nk - 2 - kt : STAGES - 2;
+          wait_stages<kLoadsPerStage, STAGES - 2>(later);
+          raw_barrier();
+          read_frags((kt + 1) % STAGES, 0, F[(s + 1) & 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int x = 0; x < NI; ++x)
+#pragma unroll
+          for (int y = 0; y < NJ; ++y) acc[x][y] = mfma(F[s & 1][x], F[s & 1][NI + y], acc[x][y]);
+        __builtin_amdgcn_sched_barrier(0);
+        // refill the buffer of stage kt once every wave is past its reads
+        // (the barrier above), behind the MFMAs just queued
+        if (last && kt + 1 < nk && kt + STAGES < nk) issue(kt + STAGES, buf);
+      }
     }
   }
 

@@ -42,56 +42,17 @@ enum Mode { kRotate = 0, kFold = 1 };
 // LDS position (in 16-byte units) of chunk c (0..15) of block b.
 __device__ __forceinline__ int lds_chunk(int b, int c) { return (b << 4) | (c ^ (b & 7)); }
 
+// Quantize one staged span: read the lane's 64 values from LDS, rotate (or
+// fold the column scale), reduce the row maxima, quantize and store.
 template <int MODE>
-__global__ __launch_bounds__(512) void rotate_quant_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int K, int8_t* __restrict__ q,
-    float* __restrict__ scale, const float* __restrict__ colscale, int rows_per_wave,
-    int waves_per_row) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ float row_part_max[kMaxWavesPerRow];
-  __shared__ float seg_max[4][kSpanBlocks];
-
+__device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_blocks, int nb,
+                                              int64_t span_elem0, int blk_in_row0, int64_t row0,
+                                              int waves_per_row, int8_t* __restrict__ q,
+                                              float* __restrict__ scale,
+                                              const float* __restrict__ colscale,
+                                              float* seg_max_wave, float* row_part_max) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nb = K / kBlock;
-
-  // ---- work assignment -------------------------------------------------
-  int64_t row0;        // first row touched by this wave
-  int span_blocks;     // blocks in this wave's span (0 = idle wave)
-  int64_t span_elem0;  // element offset of the span in x / q
-  int blk_in_row0;     // block index within the row of the span's first block
-  if (waves_per_row == 1) {
-    int64_t task = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
-    row0 = task * rows_per_wave;
-    int64_t rh = rows - row0;
-    int rows_here = rh <= 0 ? 0 : (rh < rows_per_wave ? (int)rh : rows_per_wave);
-    span_blocks = rows_here * nb;
-    span_elem0 = row0 * (int64_t)K;
-    blk_in_row0 = 0;
-  } else {
-    row0 = blockIdx.x;
-    blk_in_row0 = wave * kSpanBlocks;
-    int rem = nb - blk_in_row0;
-    span_blocks = rem < kSpanBlocks ? rem : kSpanBlocks;
-    span_elem0 = row0 * (int64_t)K + (int64_t)blk_in_row0 * kBlock;
-  }
-
-  uint8_t* my_lds = lds + wave * kSpanBytes;
-
-  // ---- stage the span in LDS (coalesced 1 KB per instruction) ------------
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int slot = i * 64 + lane;          // destination 16-byte slot
-    int b = slot >> 4;
-    int c = (slot & 15) ^ (b & 7);     // source chunk stored in that slot
-    if (b < span_blocks) {
-      const uint16_t* src = x + span_elem0 + (int64_t)b * kBlock + c * 8;
-      load_lds_16(src, my_lds + i * 1024);
-    }
-  }
-  wait_vmem();
-  __syncthreads();
-
   const int p = lane & 31;   // block within the span
   const int h = lane >> 5;   // which half of the block
   const bool active = p < span_blocks;
@@ -174,12 +135,12 @@ __global__ __launch_bounds__(512) void rotate_quant_kernel(
     if ((nb & (nb - 1)) == 0) {
       m = wave_max_xor(m, nb);             // aligned segments of nb lanes
     } else {
-      if (lane < 32) seg_max[wave][lane] = m;
+      if (lane < 32) seg_max_wave[lane] = m;
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       int first = (p / nb) * nb;
       float mm = 0.f;
-      for (int j = 0; j < nb; ++j) mm = fmaxf(mm, seg_max[wave][(first + j) & 31]);
+      for (int j = 0; j < nb; ++j) mm = fmaxf(mm, seg_max_wave[(first + j) & 31]);
       m = mm;
     }
   } else {
@@ -196,17 +157,21 @@ __global__ __launch_bounds__(512) void rotate_quant_kernel(
   const float inv = s > 0.f ? 1.0f / s : 0.f;          // RN(1/s)
 
   // ---- quantize + store --------------------------------------------------------
+  // Quotients: the 3-operation correctly rounded form when every lane's row
+  // scale is in range (wave-uniform branch), else the IEEE division per lane.
+  float t[64];
+  if (__builtin_amdgcn_ballot_w64(!fast) == 0) {
+#pragma unroll
+    for (int e = 0; e < 64; ++e) t[e] = quot_rn(r[e], s, inv);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 64; ++e) t[e] = fast ? quot_rn(r[e], s, inv) : (s > 0.f ? r[e] / s : 0.f);
+  }
   uint32_t packed[16];
 #pragma unroll
   for (int g = 0; g < 16; ++g) {
-    uint32_t bts[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float rv = r[4 * g + j];
-      float t = fast ? quot_rn(rv, s, inv) : (s > 0.f ? rv / s : 0.f);
-      bts[j] = rne_low_byte_bits(t);
-    }
-    packed[g] = pack_low_bytes(bts[0], bts[1], bts[2], bts[3]);
+    packed[g] = pack_low_bytes(rne_low_byte_bits(t[4 * g]), rne_low_byte_bits(t[4 * g + 1]),
+                               rne_low_byte_bits(t[4 * g + 2]), rne_low_byte_bits(t[4 * g + 3]));
   }
   if (active) {
     int8_t* dst = q + span_elem0 + (int64_t)p * kBlock;
@@ -221,6 +186,92 @@ __global__ __launch_bounds__(512) void rotate_quant_kernel(
     bool writes_scale = waves_per_row == 1 ? (h == 0 && p % nb == 0) : (wave == 0 && lane == 0);
     if (writes_scale) scale[row0 + (waves_per_row == 1 ? p / nb : 0)] = s;
   }
+}
+
+// Issue the 8 direct-to-LDS loads of a span of span_blocks (>= 1) blocks.
+// Slots past the span reload its last chunk so every lane always issues the
+// same number of loads (the vmcnt bookkeeping relies on it).
+__device__ __forceinline__ void stage_span(const uint16_t* __restrict__ x, int64_t span_elem0,
+                                           int span_blocks, uint8_t* my_lds) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_u32(my_lds));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int slot = i * 64 + lane;
+    int b = slot >> 4;
+    int c = (slot & 15) ^ (b & 7);
+    if (b >= span_blocks) { b = span_blocks - 1; c = 15; }
+    dma16(x + span_elem0 + (int64_t)b * kBlock + c * 8, base + i * 1024);
+  }
+}
+
+// Short rows (K <= 4096): persistent waves, each owning a task of
+// rows_per_wave packed rows at a time; the next task's span is loaded into the
+// second LDS buffer while the current one is quantized.
+template <int MODE>
+__global__ __launch_bounds__(256) void rotate_quant_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int K, int8_t* __restrict__ q,
+    float* __restrict__ scale, const float* __restrict__ colscale, int rows_per_wave) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ float seg_max[4][kSpanBlocks];
+  const int wave = threadIdx.x >> 6;
+  const int nb = K / kBlock;
+  const int64_t ntasks = (rows + rows_per_wave - 1) / rows_per_wave;
+  const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6);
+  uint8_t* bufs = lds + wave * 2 * kSpanBytes;
+  auto span_of = [&](int64_t task, int64_t& row0, int& blocks) {
+    row0 = task * rows_per_wave;
+    const int64_t rh = rows - row0;
+    blocks = (rh < rows_per_wave ? (int)rh : rows_per_wave) * nb;
+  };
+  int64_t task = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  if (task < ntasks) {
+    int64_t r0;
+    int nbk;
+    span_of(task, r0, nbk);
+    stage_span(x, r0 * (int64_t)K, nbk, bufs);
+  }
+  int cur = 0;
+  for (; task < ntasks; task += wstride) {
+    const int64_t next = task + wstride;
+    if (next < ntasks) {
+      int64_t r1;
+      int nb1;
+      span_of(next, r1, nb1);
+      stage_span(x, r1 * (int64_t)K, nb1, bufs + (cur ^ 1) * kSpanBytes);
+      wait_vm_n<8>();
+    } else {
+      wait_vm_n<0>();
+    }
+    int64_t r0;
+    int nbk;
+    span_of(task, r0, nbk);
+    quantize_span<MODE>(bufs + cur * kSpanBytes, nbk, nb, r0 * (int64_t)K, 0, r0, 1, q, scale,
+                        colscale, seg_max[wave], nullptr);
+    cur ^= 1;
+  }
+}
+
+// Long rows (K > 4096): one row per workgroup, one 4096-wide slice per wave;
+// the waves combine their maxima through LDS.
+template <int MODE>
+__global__ __launch_bounds__(512) void rotate_quant_long_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int K, int8_t* __restrict__ q,
+    float* __restrict__ scale, const float* __restrict__ colscale, int waves_per_row) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ float row_part_max[kMaxWavesPerRow];
+  const int wave = threadIdx.x >> 6;
+  const int nb = K / kBlock;
+  const int64_t row0 = blockIdx.x;
+  const int blk_in_row0 = wave * kSpanBlocks;
+  const int rem = nb - blk_in_row0;
+  const int span_blocks = rem < kSpanBlocks ? rem : kSpanBlocks;
+  const int64_t span_elem0 = row0 * (int64_t)K + (int64_t)blk_in_row0 * kBlock;
+  uint8_t* my_lds = lds + wave * kSpanBytes;
+  stage_span(x, span_elem0, span_blocks, my_lds);
+  wait_vm_n<0>();
+  quantize_span<MODE>(my_lds, span_blocks, nb, span_elem0, blk_in_row0, row0, waves_per_row, q,
+                      scale, colscale, nullptr, row_part_max);
 }
 
 }  // namespace
@@ -244,32 +295,43 @@ hipError_t launch_rotate_quant(const uint16_t* x, int64_t rows, int K, int8_t* q
                                const float* colscale, bool fold, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   RowPlan pl = plan_rows(K);
-  int64_t grid;
-  if (pl.waves_per_row == 1) {
-    int64_t waves = (rows + pl.rows_per_wave - 1) / pl.rows_per_wave;
-    grid = (waves + 3) / 4;
-  } else {
-    grid = rows;
-  }
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  size_t lds = (size_t)(pl.threads / 64) * kSpanBytes;
+  static int n_cu = 0;
   static bool configured = false;
   if (!configured) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
     const int max_lds = kMaxWavesPerRow * kSpanBytes;
-    hipError_t e0 = hipFuncSetAttribute((const void*)rotate_quant_kernel<kRotate>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-    hipError_t e1 = hipFuncSetAttribute((const void*)rotate_quant_kernel<kFold>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-    if (e0 != hipSuccess) return e0;
-    if (e1 != hipSuccess) return e1;
+    const void* ks[2] = {(const void*)rotate_quant_long_kernel<kRotate>,
+                         (const void*)rotate_quant_long_kernel<kFold>};
+    for (const void* k : ks) {
+      e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+      if (e != hipSuccess) return e;
+    }
     configured = true;
   }
-  if (fold) {
-    hipLaunchKernelGGL(rotate_quant_kernel<kFold>, dim3((unsigned)grid), dim3(pl.threads), lds,
-                       stream, x, rows, K, q, scale, colscale, pl.rows_per_wave, pl.waves_per_row);
+  if (pl.waves_per_row == 1) {
+    const int64_t tasks = (rows + pl.rows_per_wave - 1) / pl.rows_per_wave;
+    int64_t grid = (tasks + 3) / 4;
+    const int64_t cap = 2 * (int64_t)(n_cu > 0 ? n_cu : 256);  // two resident workgroups per CU
+    if (grid > cap) grid = cap;
+    const size_t lds = 4 * 2 * kSpanBytes;
+    if (fold)
+      hipLaunchKernelGGL(rotate_quant_rows_kernel<kFold>, dim3((unsigned)grid), dim3(256), lds,
+                         stream, x, rows, K, q, scale, colscale, pl.rows_per_wave);
+    else
+      hipLaunchKernelGGL(rotate_quant_rows_kernel<kRotate>, dim3((unsigned)grid), dim3(256), lds,
+                         stream, x, rows, K, q, scale, colscale, pl.rows_per_wave);
   } else {
-    hipLaunchKernelGGL(rotate_quant_kernel<kRotate>, dim3((unsigned)grid), dim3(pl.threads), lds,
-                       stream, x, rows, K, q, scale, colscale, pl.rows_per_wave, pl.waves_per_row);
+    if (rows > 0x7fffffff) return hipErrorInvalidValue;
+    const size_t lds = (size_t)pl.waves_per_row * kSpanBytes;
+    if (fold)
+      hipLaunchKernelGGL(rotate_quant_long_kernel<kFold>, dim3((unsigned)rows), dim3(pl.threads),
+                         lds, stream, x, rows, K, q, scale, colscale, pl.waves_per_row);
+    else
+      hipLaunchKernelGGL(rotate_quant_long_kernel<kRotate>, dim3((unsigned)rows), dim3(pl.threads),
+                         lds, stream, x, rows, K, q, scale, colscale, pl.waves_per_row);
   }
   return hipGetLastError();
 }
