@@ -55,22 +55,39 @@ __device__ __forceinline__ void fwht_codes(const uint4 raw[4], float w[64]) {
 // LDS position (16-byte units) of chunk c (0..7) of int8 block b.
 __device__ __forceinline__ int lds_chunk8(int b, int c) { return (b << 3) | (c ^ (b & 7)); }
 
-// Store the 64 outputs of this lane's half block (see fwht_codes) scaled by rs.
-__device__ __forceinline__ void store_block_half(uint16_t* blk_out, int h, const float w[64],
-                                                 float rs) {
-  uint4* d0 = reinterpret_cast<uint4*>(blk_out + 32 * h);
-  uint4* d1 = reinterpret_cast<uint4*>(blk_out + 64 + 32 * h);
+// Store the bf16 outputs of a span of `span` blocks (this lane holds 64 of
+// them, see fwht_codes) scaled by rs: staged in LDS (8 KB per wave), then
+// written as whole 1 KB runs (lane i of step j writes 16-byte chunk 64j + i).
+// Chunk c of block c/16 sits at c ^ (c/16 & 15) (conflict-free writes).
+__device__ __forceinline__ void store_span(uint16_t* span_out, int span, const float w[64],
+                                           float rs, uint8_t* stg) {
+  const int lane = threadIdx.x & 63;
+  const int p = lane & 31, h = lane >> 5;
+  auto phys = [](int c) { return c ^ ((c >> 4) & 15); };
+  if (p < span) {
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    d0[g] = make_uint4(pack_bf16x2(w[8 * g] * rs, w[8 * g + 1] * rs),
-                       pack_bf16x2(w[8 * g + 2] * rs, w[8 * g + 3] * rs),
-                       pack_bf16x2(w[8 * g + 4] * rs, w[8 * g + 5] * rs),
-                       pack_bf16x2(w[8 * g + 6] * rs, w[8 * g + 7] * rs));
-    d1[g] = make_uint4(pack_bf16x2(w[32 + 8 * g] * rs, w[32 + 8 * g + 1] * rs),
-                       pack_bf16x2(w[32 + 8 * g + 2] * rs, w[32 + 8 * g + 3] * rs),
-                       pack_bf16x2(w[32 + 8 * g + 4] * rs, w[32 + 8 * g + 5] * rs),
-                       pack_bf16x2(w[32 + 8 * g + 6] * rs, w[32 + 8 * g + 7] * rs));
+    for (int run = 0; run < 2; ++run) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float* v = w + 32 * run + 8 * g;
+        const int c = 16 * p + 8 * run + 4 * h + g;
+        *reinterpret_cast<uint4*>(stg + 16 * phys(c)) =
+            make_uint4(pack_bf16x2(v[0] * rs, v[1] * rs), pack_bf16x2(v[2] * rs, v[3] * rs),
+                       pack_bf16x2(v[4] * rs, v[5] * rs), pack_bf16x2(v[6] * rs, v[7] * rs));
+      }
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staging writes landed
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+  const int nchunks = span * 16;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = 64 * j + lane;
+    if (c < nchunks)
+      *reinterpret_cast<uint4*>(span_out + 8 * c) = *reinterpret_cast<const uint4*>(stg + 16 * phys(c));
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // staging reads retired before it is reused
 }
 
 // Issue the 4 direct-to-LDS loads of a row span of span (1..32) int8 blocks;
@@ -97,6 +114,7 @@ __global__ __launch_bounds__(256) void embedding_lookup_kernel(
     const float* __restrict__ se, int64_t V, int D, uint16_t* __restrict__ out,
     int32_t* __restrict__ oob) {
   __shared__ __align__(16) uint8_t lds[4][2][4096];
+  __shared__ __align__(16) uint8_t stage_out[4][8192];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = lane & 31, h = lane >> 5;
   const int span = D / kBlock;
@@ -146,7 +164,7 @@ __global__ __launch_bounds__(256) void embedding_lookup_kernel(
                      : make_uint4(0, 0, 0, 0);
     float w[64];
     fwht_codes(raw, w);
-    if (p < span) store_block_half(out + t * (int64_t)D + (int64_t)p * kBlock, h, w, rs);
+    store_span(out + t * (int64_t)D, span, w, rs, stage_out[wave]);
     id = nid;
     rs = nrs;
     cur ^= 1;
@@ -159,6 +177,7 @@ __global__ __launch_bounds__(256) void embedding_lookup_long_kernel(
     const float* __restrict__ se, int64_t V, int D, uint16_t* __restrict__ out,
     int32_t* __restrict__ oob) {
   __shared__ __align__(16) uint8_t lds[4][4096];
+  __shared__ __align__(16) uint8_t stage_out[4][8192];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= T) return;
@@ -180,7 +199,7 @@ __global__ __launch_bounds__(256) void embedding_lookup_long_kernel(
     __builtin_amdgcn_s_waitcnt(0xc07f);  // LDS reads retired before the next span overwrites
     float w[64];
     fwht_codes(raw, w);
-    if (p < span) store_block_half(out + t * (int64_t)D + (int64_t)(b0 + p) * kBlock, h, w, rs);
+    store_span(out + t * (int64_t)D + (int64_t)b0 * kBlock, span, w, rs, stage_out[wave]);
   }
 }
 

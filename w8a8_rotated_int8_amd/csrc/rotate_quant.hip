@@ -173,18 +173,32 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
     packed[g] = pack_low_bytes(rne_low_byte_bits(t[4 * g]), rne_low_byte_bits(t[4 * g + 1]),
                                rne_low_byte_bits(t[4 * g + 2]), rne_low_byte_bits(t[4 * g + 3]));
   }
+  // Stage the codes of the span in LDS (its own input buffer, already read)
+  // and store whole 1 KB runs: lane i of step j writes 16-byte chunk 64j + i.
+  // Chunk c of block c/8 sits at c ^ (c/8 & 7) (conflict-free writes).
+  uint8_t* stg = const_cast<uint8_t*>(my_lds);
+  auto phys = [](int c) { return c ^ ((c >> 3) & 7); };
   if (active) {
-    int8_t* dst = q + span_elem0 + (int64_t)p * kBlock;
-    int off0 = MODE == kRotate ? 32 * h : 64 * h;        // values e = 0..31
-    int off1 = MODE == kRotate ? 64 + 32 * h : 64 * h + 32;  // values e = 32..63
-    uint4* d0 = reinterpret_cast<uint4*>(dst + off0);
-    uint4* d1 = reinterpret_cast<uint4*>(dst + off1);
-    d0[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    d0[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-    d1[0] = make_uint4(packed[8], packed[9], packed[10], packed[11]);
-    d1[1] = make_uint4(packed[12], packed[13], packed[14], packed[15]);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = MODE == kRotate ? 8 * p + (g < 2 ? 2 * h + g : 4 + 2 * h + (g - 2))
+                                    : 8 * p + 4 * h + g;
+      *reinterpret_cast<uint4*>(stg + 16 * phys(c)) =
+          make_uint4(packed[4 * g], packed[4 * g + 1], packed[4 * g + 2], packed[4 * g + 3]);
+    }
     bool writes_scale = waves_per_row == 1 ? (h == 0 && p % nb == 0) : (wave == 0 && lane == 0);
     if (writes_scale) scale[row0 + (waves_per_row == 1 ? p / nb : 0)] = s;
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staging writes landed
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+  const int nchunks = span_blocks * 8;
+  int8_t* dst = q + span_elem0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = 64 * j + lane;
+    if (c < nchunks)
+      *reinterpret_cast<uint4*>(dst + 16 * c) = *reinterpret_cast<const uint4*>(stg + 16 * phys(c));
   }
 }
 
