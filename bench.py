@@ -47,7 +47,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", default="all", choices=["all", "fwd", "kernels"])
+    ap.add_argument("--only", default="all", choices=["all", "fwd", "copy"],
+                    help="fwd: headline only; copy: a plain 1 GiB device copy (calibrates "
+                         "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -69,6 +71,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cr.lib()
+
+    if args.only == "copy":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied 3 x 1 GiB (counter calibration: 1073741824 bytes read and written per copy)")
+        return
 
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
