@@ -45,8 +45,12 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # The GPU's clocks ramp up over the first ~35 ms of continuous work (one
+    # linear_fwd call takes ~112 us cold and ~83 us once ramped), so the default
+    # warmup covers ~80 ms of calls and the timed region is long enough to be
+    # insensitive to the ramp's tail.
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--only", default="all", choices=["all", "fwd", "copy"],
                     help="fwd: headline only; copy: a plain 1 GiB device copy (calibrates "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes)")
@@ -84,10 +88,17 @@ def main():
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    def time_ms(fn, warmup, iters):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
+    def time_ms(fn, warmup, iters, min_warm_s=0.08):
+        # at least `warmup` calls and at least min_warm_s of back-to-back calls
+        # (batches of calls with one synchronization each), so that every
+        # measurement starts from ramped clocks even after host-side setup
+        t0 = time.perf_counter()
+        n = 0
+        while n < warmup or time.perf_counter() - t0 < min_warm_s:
+            for _ in range(max(1, min(warmup, 16))):
+                fn()
+                n += 1
+            torch.cuda.synchronize()
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         s.record()

@@ -28,6 +28,8 @@
 // the 8 XCDs round-robin, so consecutive dispatch ids are first regrouped per
 // XCD, and each XCD then walks a compact block of tiles (GROUP_J j-tiles wide)
 // whose P and Q rows are shared through that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -336,14 +338,20 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
       raw_barrier();
     }
     read_frags(0, 0, F[0]);
-    for (int kt = 0; kt < nk; ++kt) {
+    // One stage.  HAS_NEXT is a compile-time flag (the final stage is peeled
+    // off the loop) so that no control-flow join sits between the fragment
+    // reads of stage kt+1 and the MFMAs of stage kt's last slice: at such a
+    // join the waitcnt insertion becomes conservative and would make those
+    // MFMAs wait for the reads just issued.
+    auto stage = [&](int kt, auto has_next) {
+      constexpr bool HAS_NEXT = decltype(has_next)::value;
       const int buf = kt % STAGES;
 #pragma unroll
       for (int s = 0; s < SL; ++s) {
         const bool last = s + 1 == SL;
         if (!last) {
           read_frags(buf, s + 1, F[(s + 1) & 1]);
-        } else if (kt + 1 < nk) {
+        } else if constexpr (HAS_NEXT) {
           // Retire this wave's reads of stage kt, wait for stage kt+1 (at most
           // min(STAGES-2, nk-2-kt) later stages in flight) and publish; the
           // MFMAs of earlier slices keep the matrix pipe busy meanwhile.
@@ -361,9 +369,13 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         // refill the buffer of stage kt once every wave is past its reads
         // (the barrier above), behind the MFMAs just queued
-        if (last && kt + 1 < nk && kt + STAGES < nk) issue(kt + STAGES, buf);
+        if constexpr (HAS_NEXT) {
+          if (last && kt + STAGES < nk) issue(kt + STAGES, buf);
+        }
       }
-    }
+    };
+    for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, std::true_type{});
+    if (nk > 0) stage(nk - 1, std::false_type{});
   }
 
   // ---- epilogue -------------------------------------------------------------
