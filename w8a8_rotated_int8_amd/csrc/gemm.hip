@@ -343,6 +343,27 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
     // reads of stage kt+1 and the MFMAs of stage kt's last slice: at such a
     // join the waitcnt insertion becomes conservative and would make those
     // MFMAs wait for the reads just issued.
+    // MFMAs of slice s with the fragment reads of the next slice interleaved
+    // one read per MFMA, so neither wave of a SIMD issues a burst of reads
+    // while the matrix pipe waits.
+    auto mfma_slice = [&](int s) {
+#pragma unroll
+      for (int x = 0; x < NI; ++x)
+#pragma unroll
+        for (int y = 0; y < NJ; ++y) acc[x][y] = mfma(F[s & 1][x], F[s & 1][NI + y], acc[x][y]);
+#pragma unroll
+      for (int i = 0; i < NI + NJ; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NI * NJ - (NI + NJ), 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // One stage.  HAS_NEXT is a compile-time flag (the final stage is peeled
+    // off the loop) so that no control-flow join sits between the fragment
+    // reads of stage kt+1 and the MFMAs of stage kt's last slice: at such a
+    // join the waitcnt insertion becomes conservative and would make those
+    // MFMAs wait for the reads just issued.
     auto stage = [&](int kt, auto has_next) {
       constexpr bool HAS_NEXT = decltype(has_next)::value;
       const int buf = kt % STAGES;
@@ -351,6 +372,7 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
         const bool last = s + 1 == SL;
         if (!last) {
           read_frags(buf, s + 1, F[(s + 1) & 1]);
+          mfma_slice(s);
         } else if constexpr (HAS_NEXT) {
           // Retire this wave's reads of stage kt, wait for stage kt+1 (at most
           // min(STAGES-2, nk-2-kt) later stages in flight) and publish; the
@@ -359,18 +381,19 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
           const int later = nk - 2 - kt < STAGES - 2 ? nk - 2 - kt : STAGES - 2;
           wait_stages<kLoadsPerStage, STAGES - 2>(later);
           raw_barrier();
+          __builtin_amdgcn_sched_barrier(0);
           read_frags((kt + 1) % STAGES, 0, F[(s + 1) & 1]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+          mfma_slice(s);
+          // refill the buffer of stage kt: every wave is past its reads of it
+          // (the barrier above)
+          if (kt + STAGES < nk) issue(kt + STAGES, buf);
+        } else {
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int x = 0; x < NI; ++x)
+          for (int x = 0; x < NI; ++x)
 #pragma unroll
-          for (int y = 0; y < NJ; ++y) acc[x][y] = mfma(F[s & 1][x], F[s & 1][NI + y], acc[x][y]);
-        __builtin_amdgcn_sched_barrier(0);
-        // refill the buffer of stage kt once every wave is past its reads
-        // (the barrier above), behind the MFMAs just queued
-        if constexpr (HAS_NEXT) {
-          if (last && kt + STAGES < nk) issue(kt + STAGES, buf);
+            for (int y = 0; y < NJ; ++y) acc[x][y] = mfma(F[s & 1][x], F[s & 1][NI + y], acc[x][y]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     };

@@ -22,9 +22,12 @@
 // 4096-wide slice of a long row (then the workgroup's waves share the row and
 // combine their maxima through LDS).  The span is copied to LDS with direct
 // 16-byte global->LDS loads (coalesced, XOR-swizzled so the transposed reads
-// are bank-conflict free); lane L < 32 then holds the first half (64 values) of
-// block L, lane L + 32 the second half.  Six butterfly stages run inside the
-// lane; the seventh pairs lane L with L + 32 through v_permlane32_swap.
+// are bank-conflict free) and processed in two passes of 16 blocks: in pass k
+// lane 16 g + p holds elements 32 g .. 32 g + 31 of block 16 k + p.  Five
+// butterfly stages run inside the lane, the sixth pairs lane L with L + 16
+// (v_permlane16_swap) and the seventh with L + 32 (v_permlane32_swap).  With
+// 32 values per lane a wave needs at most 128 VGPRs, so four waves share each
+// SIMD and cover each other's load latency.
 #pragma clang fp contract(off)
 
 #include "common.h"
@@ -32,6 +35,10 @@
 
 namespace convrot {
 namespace {
+
+#ifndef CONVROT_RQ_WAVES
+#define CONVROT_RQ_WAVES 2
+#endif
 
 constexpr int kSpanBlocks = 32;                  // blocks per wave span
 constexpr int kSpanBytes = kSpanBlocks * 256;    // bf16 bytes per wave span
@@ -42,8 +49,25 @@ enum Mode { kRotate = 0, kFold = 1 };
 // LDS position (in 16-byte units) of chunk c (0..15) of block b.
 __device__ __forceinline__ int lds_chunk(int b, int c) { return (b << 4) | (c ^ (b & 7)); }
 
-// Quantize one staged span: read the lane's 64 values from LDS, rotate (or
-// fold the column scale), reduce the row maxima, quantize and store.
+// Exchange with the neighbouring 16-lane row: rows 1 and 3 of vdst swap with
+// rows 0 and 2 of src0 (v_permlane16_swap).
+__device__ __forceinline__ void swap_rows16(double& vdst, double& src0) {
+  uint64_t a = __builtin_bit_cast(uint64_t, vdst), b = __builtin_bit_cast(uint64_t, src0);
+  auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)a, (uint32_t)b, false, false);
+  auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(a >> 32), (uint32_t)(b >> 32), false, false);
+  vdst = __builtin_bit_cast(double, ((uint64_t)hi[0] << 32) | lo[0]);
+  src0 = __builtin_bit_cast(double, ((uint64_t)hi[1] << 32) | lo[1]);
+}
+
+// Quantize one staged span: per pass read the lane's 32 values from LDS and
+// rotate them (or fold the column scale); then reduce the row maxima,
+// quantize, stage the codes in LDS and store them.
+//
+// Rotation data flow: the in-lane stages cover element bits 0-4 (register
+// index e).  Each cross-lane swap pairs v[e] with v[e + 16] and exchanges
+// register bit 4 with a lane bit, so that the butterfly partners meet in one
+// lane.  After both, lane quarter q = L >> 4 holds outputs 16 q + e in v[e]
+// and 64 + 16 q + e in v[e + 16] (e < 16).
 template <int MODE>
 __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_blocks, int nb,
                                               int64_t span_elem0, int blk_in_row0, int64_t row0,
@@ -53,141 +77,174 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
                                               float* seg_max_wave, float* row_part_max) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int p = lane & 31;   // block within the span
-  const int h = lane >> 5;   // which half of the block
-  const bool active = p < span_blocks;
+  const int p = lane & 15;   // block within the pass
+  const int g = lane >> 4;   // which quarter of the block
 
-  // ---- read the lane's 64 values ------------------------------------------
-  uint4 raw[8];
+  float r[2][32];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    raw[i] = *reinterpret_cast<const uint4*>(my_lds + 16 * lds_chunk(p, 8 * h + i));
-  }
-
-  float r[64];
-  if (MODE == kRotate) {
-    double v[64];
+  for (int k = 0; k < 2; ++k) {
+    // keep the two passes apart: interleaving them would hold both passes'
+    // binary64 working sets at once
+    __builtin_amdgcn_sched_barrier(0);
+    const int b = 16 * k + p;
+    const bool active = b < span_blocks;
+    if (k == 1 && span_blocks <= 16) {  // wave-uniform: the span fits in one pass
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+      for (int e = 0; e < 32; ++e) r[1][e] = 0.f;
+      continue;
+    }
+    uint4 raw[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j] = (double)bf16lo_to_f32(w[j]);
-        v[8 * i + 2 * j + 1] = (double)bf16hi_to_f32(w[j]);
+    for (int i = 0; i < 4; ++i)
+      raw[i] = *reinterpret_cast<const uint4*>(my_lds + 16 * lds_chunk(b, 4 * g + i));
+    if (MODE == kRotate) {
+      double v[32];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * i + 2 * j] = (double)bf16lo_to_f32(w[j]);
+          v[8 * i + 2 * j + 1] = (double)bf16hi_to_f32(w[j]);
+        }
       }
-    }
-    if (!active) {
+      if (!active) {
 #pragma unroll
-      for (int e = 0; e < 64; ++e) v[e] = 0.0;
-    }
-    // in-lane butterflies over index bits 0..5 (element 64h + e of the block)
-#pragma unroll
-    for (int bit = 1; bit < 64; bit <<= 1) {
-#pragma unroll
-      for (int e = 0; e < 64; ++e) {
-        if (e & bit) continue;
-        double a = v[e], b = v[e | bit];
-        v[e] = a + b;
-        v[e | bit] = a - b;
+        for (int e = 0; e < 32; ++e) v[e] = 0.0;
       }
-    }
-    // bit 6 pairs lane L with lane L + 32.  After the swap the lower lane holds
-    // (A[e], B[e]) and the upper lane (A[e+32], B[e+32]) in (v[e], v[e+32]).
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      swap_halves(v[e], v[e + 32]);
-      double a = v[e], b = v[e + 32];
-      v[e] = a + b;        // output index 32h + e
-      v[e + 32] = a - b;   // output index 64 + 32h + e
-    }
+      for (int bit = 1; bit < 32; bit <<= 1) {
 #pragma unroll
-    for (int e = 0; e < 64; ++e) r[e] = (float)(v[e] * kInvSqrt128);
-  } else {
-    // fold the per-column scale: element 64h + e of block p
-    const int64_t col0 = active ? (int64_t)(blk_in_row0 + (waves_per_row == 1 ? p % nb : p)) * kBlock +
-                                      64 * h
-                                : 0;
-    const float4* cs = reinterpret_cast<const float4*>(colscale + col0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-      float4 s0 = active ? cs[2 * i] : make_float4(0.f, 0.f, 0.f, 0.f);
-      float4 s1 = active ? cs[2 * i + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
-      float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        r[8 * i + 2 * j] = bf16lo_to_f32(w[j]) * sc[2 * j];
-        r[8 * i + 2 * j + 1] = bf16hi_to_f32(w[j]) * sc[2 * j + 1];
+        for (int e = 0; e < 32; ++e) {
+          if (e & bit) continue;
+          double a = v[e], c = v[e | bit];
+          v[e] = a + c;
+          v[e | bit] = a - c;
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one stage at a time (register pressure)
       }
-    }
-    if (!active) {
+      // element bit 5: lane L with L + 16
 #pragma unroll
-      for (int e = 0; e < 64; ++e) r[e] = 0.f;
+      for (int e = 0; e < 16; ++e) {
+        swap_rows16(v[e], v[e + 16]);
+        double a = v[e], c = v[e + 16];
+        v[e] = a + c;
+        v[e + 16] = a - c;
+      }
+      // element bit 6: lane L with L + 32
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        swap_halves(v[e], v[e + 16]);
+        double a = v[e], c = v[e + 16];
+        v[e] = a + c;
+        v[e + 16] = a - c;
+      }
+#pragma unroll
+      for (int e = 0; e < 32; ++e) r[k][e] = (float)(v[e] * kInvSqrt128);
+    } else {
+      // fold the per-column scale: element 32 g + e of block b
+      const int64_t col0 =
+          active ? (int64_t)(blk_in_row0 + (waves_per_row == 1 ? b % nb : b)) * kBlock + 32 * g
+                 : 0;
+      const float4* cs = reinterpret_cast<const float4*>(colscale + col0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+        float4 s0 = active ? cs[2 * i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 s1 = active ? cs[2 * i + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+        float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          r[k][8 * i + 2 * j] = bf16lo_to_f32(w[j]) * sc[2 * j];
+          r[k][8 * i + 2 * j + 1] = bf16hi_to_f32(w[j]) * sc[2 * j + 1];
+        }
+      }
+      if (!active) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) r[k][e] = 0.f;
+      }
     }
   }
 
   // ---- row absmax ------------------------------------------------------------
-  float m = 0.f;
+  float m[2] = {0.f, 0.f};
 #pragma unroll
-  for (int e = 0; e < 64; ++e) m = fmaxf(m, fabsf(r[e]));
-  m = fmaxf(m, __shfl_xor(m, 32, kWave));  // both halves of the block
+  for (int k = 0; k < 2; ++k) {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) m[k] = fmaxf(m[k], fabsf(r[k][e]));
+    m[k] = fmaxf(m[k], __shfl_xor(m[k], 16, kWave));  // the four quarters of the block
+    m[k] = fmaxf(m[k], __shfl_xor(m[k], 32, kWave));
+  }
   if (waves_per_row == 1) {
-    if ((nb & (nb - 1)) == 0) {
-      m = wave_max_xor(m, nb);             // aligned segments of nb lanes
+    if (nb == 32) {
+      const float mm = wave_max_xor(fmaxf(m[0], m[1]), 16);
+      m[0] = m[1] = mm;
+    } else if ((nb & (nb - 1)) == 0) {
+      m[0] = wave_max_xor(m[0], nb);       // aligned segments of nb blocks
+      m[1] = wave_max_xor(m[1], nb);
     } else {
-      if (lane < 32) seg_max_wave[lane] = m;
+      if (g == 0) {
+        seg_max_wave[p] = m[0];
+        seg_max_wave[16 + p] = m[1];
+      }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      int first = (p / nb) * nb;
-      float mm = 0.f;
-      for (int j = 0; j < nb; ++j) mm = fmaxf(mm, seg_max_wave[(first + j) & 31]);
-      m = mm;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int first = ((16 * k + p) / nb) * nb;
+        float mm = 0.f;
+        for (int j = 0; j < nb; ++j) {
+          const int idx = first + j;
+          if (idx < kSpanBlocks) mm = fmaxf(mm, seg_max_wave[idx]);
+        }
+        m[k] = mm;
+      }
     }
   } else {
-    m = wave_max_xor(m, 32);
-    if (lane == 0) row_part_max[wave] = m;
+    const float mw = wave_max_xor(fmaxf(m[0], m[1]), 16);
+    if (lane == 0) row_part_max[wave] = mw;
     __syncthreads();
     float mm = 0.f;
     for (int w = 0; w < waves_per_row; ++w) mm = fmaxf(mm, row_part_max[w]);
-    m = mm;
+    m[0] = m[1] = mm;
   }
 
-  const float s = m / 127.0f;                          // IEEE binary32 division
-  const bool fast = s > 0x1p-100f && s < 0x1p100f;
-  const float inv = s > 0.f ? 1.0f / s : 0.f;          // RN(1/s)
-
-  // ---- quantize + store --------------------------------------------------------
-  // Quotients: the 3-operation correctly rounded form when every lane's row
-  // scale is in range (wave-uniform branch), else the IEEE division per lane.
-  float t[64];
-  if (__builtin_amdgcn_ballot_w64(!fast) == 0) {
-#pragma unroll
-    for (int e = 0; e < 64; ++e) t[e] = quot_rn(r[e], s, inv);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 64; ++e) t[e] = fast ? quot_rn(r[e], s, inv) : (s > 0.f ? r[e] / s : 0.f);
-  }
-  uint32_t packed[16];
-#pragma unroll
-  for (int g = 0; g < 16; ++g) {
-    packed[g] = pack_low_bytes(rne_low_byte_bits(t[4 * g]), rne_low_byte_bits(t[4 * g + 1]),
-                               rne_low_byte_bits(t[4 * g + 2]), rne_low_byte_bits(t[4 * g + 3]));
-  }
-  // Stage the codes of the span in LDS (its own input buffer, already read)
-  // and store whole 1 KB runs: lane i of step j writes 16-byte chunk 64j + i.
+  // ---- quantize + stage + store -------------------------------------------------
+  // Codes are staged in LDS (the span's own input buffer, already read) and
+  // stored as whole 1 KB runs: lane i of step j writes 16-byte chunk 64 j + i.
   // Chunk c of block c/8 sits at c ^ (c/8 & 7) (conflict-free writes).
   uint8_t* stg = const_cast<uint8_t*>(my_lds);
   auto phys = [](int c) { return c ^ ((c >> 3) & 7); };
-  if (active) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int c = MODE == kRotate ? 8 * p + (g < 2 ? 2 * h + g : 4 + 2 * h + (g - 2))
-                                    : 8 * p + 4 * h + g;
-      *reinterpret_cast<uint4*>(stg + 16 * phys(c)) =
-          make_uint4(packed[4 * g], packed[4 * g + 1], packed[4 * g + 2], packed[4 * g + 3]);
+  for (int k = 0; k < 2; ++k) {
+    const int b = 16 * k + p;
+    const float s = m[k] / 127.0f;                     // IEEE binary32 division
+    const bool fast = s > 0x1p-100f && s < 0x1p100f;
+    const float inv = s > 0.f ? 1.0f / s : 0.f;        // RN(1/s)
+    // Quotients: the 3-operation correctly rounded form when every lane's row
+    // scale is in range (wave-uniform branch), else the IEEE division per lane.
+    float t[32];
+    if (__builtin_amdgcn_ballot_w64(!fast) == 0) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) t[e] = quot_rn(r[k][e], s, inv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) t[e] = fast ? quot_rn(r[k][e], s, inv) : (s > 0.f ? r[k][e] / s : 0.f);
     }
-    bool writes_scale = waves_per_row == 1 ? (h == 0 && p % nb == 0) : (wave == 0 && lane == 0);
-    if (writes_scale) scale[row0 + (waves_per_row == 1 ? p / nb : 0)] = s;
+    uint32_t packed[8];
+#pragma unroll
+    for (int gg = 0; gg < 8; ++gg) {
+      packed[gg] = pack_low_bytes(rne_low_byte_bits(t[4 * gg]), rne_low_byte_bits(t[4 * gg + 1]),
+                                  rne_low_byte_bits(t[4 * gg + 2]), rne_low_byte_bits(t[4 * gg + 3]));
+    }
+    if (b < span_blocks) {
+      const int c_lo = 8 * b + (MODE == kRotate ? g : 2 * g);
+      const int c_hi = 8 * b + (MODE == kRotate ? 4 + g : 2 * g + 1);
+      *reinterpret_cast<uint4*>(stg + 16 * phys(c_lo)) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      *reinterpret_cast<uint4*>(stg + 16 * phys(c_hi)) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+      if (waves_per_row == 1 && g == 0 && b % nb == 0) scale[row0 + b / nb] = s;
+    }
+    if (k == 0 && waves_per_row > 1 && wave == 0 && lane == 0) scale[row0] = s;
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staging writes landed
   __builtin_amdgcn_wave_barrier();
@@ -219,11 +276,11 @@ __device__ __forceinline__ void stage_span(const uint16_t* __restrict__ x, int64
   }
 }
 
-// Short rows (K <= 4096): persistent waves, each owning a task of
-// rows_per_wave packed rows at a time; the next task's span is loaded into the
-// second LDS buffer while the current one is quantized.
+// Short rows (K <= 4096): one task of rows_per_wave packed rows per wave, in
+// its own 8 KB LDS buffer; several resident waves per SIMD cover each other's
+// load latency.
 template <int MODE>
-__global__ __launch_bounds__(256) void rotate_quant_rows_kernel(
+__global__ __launch_bounds__(256, CONVROT_RQ_WAVES) void rotate_quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int K, int8_t* __restrict__ q,
     float* __restrict__ scale, const float* __restrict__ colscale, int rows_per_wave) {
   extern __shared__ __align__(16) uint8_t lds[];
@@ -231,39 +288,16 @@ __global__ __launch_bounds__(256) void rotate_quant_rows_kernel(
   const int wave = threadIdx.x >> 6;
   const int nb = K / kBlock;
   const int64_t ntasks = (rows + rows_per_wave - 1) / rows_per_wave;
-  const int64_t wstride = (int64_t)gridDim.x * (blockDim.x >> 6);
-  uint8_t* bufs = lds + wave * 2 * kSpanBytes;
-  auto span_of = [&](int64_t task, int64_t& row0, int& blocks) {
-    row0 = task * rows_per_wave;
-    const int64_t rh = rows - row0;
-    blocks = (rh < rows_per_wave ? (int)rh : rows_per_wave) * nb;
-  };
-  int64_t task = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
-  if (task < ntasks) {
-    int64_t r0;
-    int nbk;
-    span_of(task, r0, nbk);
-    stage_span(x, r0 * (int64_t)K, nbk, bufs);
-  }
-  int cur = 0;
-  for (; task < ntasks; task += wstride) {
-    const int64_t next = task + wstride;
-    if (next < ntasks) {
-      int64_t r1;
-      int nb1;
-      span_of(next, r1, nb1);
-      stage_span(x, r1 * (int64_t)K, nb1, bufs + (cur ^ 1) * kSpanBytes);
-      wait_vm_n<8>();
-    } else {
-      wait_vm_n<0>();
-    }
-    int64_t r0;
-    int nbk;
-    span_of(task, r0, nbk);
-    quantize_span<MODE>(bufs + cur * kSpanBytes, nbk, nb, r0 * (int64_t)K, 0, r0, 1, q, scale,
-                        colscale, seg_max[wave], nullptr);
-    cur ^= 1;
-  }
+  const int64_t task = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  if (task >= ntasks) return;
+  uint8_t* buf = lds + wave * kSpanBytes;
+  const int64_t r0 = task * rows_per_wave;
+  const int64_t rh = rows - r0;
+  const int nbk = (rh < rows_per_wave ? (int)rh : rows_per_wave) * nb;
+  stage_span(x, r0 * (int64_t)K, nbk, buf);
+  wait_vm_n<0>();
+  quantize_span<MODE>(buf, nbk, nb, r0 * (int64_t)K, 0, r0, 1, q, scale, colscale,
+                      seg_max[wave], nullptr);
 }
 
 // Long rows (K > 4096): one row per workgroup, one 4096-wide slice per wave;
@@ -327,10 +361,9 @@ hipError_t launch_rotate_quant(const uint16_t* x, int64_t rows, int K, int8_t* q
   }
   if (pl.waves_per_row == 1) {
     const int64_t tasks = (rows + pl.rows_per_wave - 1) / pl.rows_per_wave;
-    int64_t grid = (tasks + 3) / 4;
-    const int64_t cap = 2 * (int64_t)(n_cu > 0 ? n_cu : 256);  // two resident workgroups per CU
-    if (grid > cap) grid = cap;
-    const size_t lds = 4 * 2 * kSpanBytes;
+    const int64_t grid = (tasks + 3) / 4;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    const size_t lds = 4 * kSpanBytes;
     if (fold)
       hipLaunchKernelGGL(rotate_quant_rows_kernel<kFold>, dim3((unsigned)grid), dim3(256), lds,
                          stream, x, rows, K, q, scale, colscale, pl.rows_per_wave);
