@@ -182,6 +182,7 @@ def main():
     del x, w, ws, y, y2, qx, sx
 
     if args.only == "all":
+        extra.update(bench_qkv(cr, torch, dev, dev_normal, time_ms, wl))
         extra.update(bench_embedding(cr, torch, dev, dev_normal, time_ms, wl))
         extra.update(bench_mlp(cr, torch, dev, dev_normal, time_ms, wl))
         extra.update(bench_packed(cr, torch, dev, dev_normal, time_ms, wl))
@@ -217,6 +218,35 @@ def gemm_traffic():
     except (OSError, ValueError):
         pass
     return None
+
+
+def bench_qkv(cr, torch, dev, dev_normal, time_ms, wl):
+    """q, k, v projections of one input: three separate forwards against one
+    forward on the stacked [3N, K] weight codes (one activation quantization)."""
+    M, K, N = 4096, 4096, 4096
+    log("[bench] shared-input q/k/v: 3 x [4096,4096] separately and stacked")
+    cols = wl.outlier_columns(K, wl.n_outliers(K), 0)
+    x = dev_normal((M, K), 1.0, 31, cols)
+    qcat = torch.empty((3 * N, K), dtype=torch.int8, device=dev)
+    scat = torch.empty((3 * N,), dtype=torch.float32, device=dev)
+    for j in range(3):
+        cr.quantize_weight(dev_normal((N, K), wl.SIGMA_W, 32 + j),
+                           out=(qcat[j * N:(j + 1) * N], scat[j * N:(j + 1) * N]))
+    y = torch.empty((M, 3 * N), dtype=torch.bfloat16, device=dev)
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    ws = torch.empty(cr.workspace_bytes(cr.OP_LINEAR_FWD, M, 3 * N, K), dtype=torch.uint8, device=dev)
+
+    def separate():
+        for j in range(3):
+            cr.linear_fwd(x, qcat[j * N:(j + 1) * N], scat[j * N:(j + 1) * N], out=ys[j], workspace=ws)
+
+    ops = 3 * 2.0 * M * N * K
+    t_sep = time_ms(separate, 10, 100)
+    t_cat = time_ms(lambda: cr.linear_fwd(x, qcat, scat, out=y, workspace=ws), 10, 100)
+    r = {"qkv_separate_us": round(t_sep * 1e3, 1), "qkv_separate_tops": round(ops / (t_sep * 1e-3) / 1e12, 1),
+         "qkv_stacked_us": round(t_cat * 1e3, 1), "qkv_stacked_tops": round(ops / (t_cat * 1e-3) / 1e12, 1)}
+    log(f"[bench] qkv {r}")
+    return r
 
 
 def bench_embedding(cr, torch, dev, dev_normal, time_ms, wl):

@@ -279,3 +279,30 @@ def test_embedding_lookup(cr, orc, V, D, T):
     ob = bits(out)
     assert not ob[0].any() and not ob[-1].any()
     assert_rows_close(ob, oout, "lookup")
+
+
+def test_binding_rejects_mismatched_buffers(cr):
+    """The binding checks every tensor against the sizes it passes to the C ABI
+    (which sees only pointers) and raises before anything is enqueued."""
+    d = "cuda"
+    x = torch.zeros((64, 256), dtype=torch.bfloat16, device=d)
+    qw = torch.zeros((128, 256), dtype=torch.int8, device=d)
+    sw = torch.ones((128,), dtype=torch.float32, device=d)
+    bad = [
+        lambda: cr.linear_fwd(x, qw, sw[:64]),                                   # scales too short
+        lambda: cr.linear_fwd(x, qw[:, :128].contiguous(), sw),                  # K mismatch
+        lambda: cr.linear_fwd(x, qw, sw, bias=torch.zeros(64, dtype=torch.bfloat16, device=d)),
+        lambda: cr.linear_fwd(x, qw, sw, out=torch.empty((64, 64), dtype=torch.bfloat16, device=d)),
+        lambda: cr.linear_fwd(x, qw, sw, workspace=torch.empty(16, dtype=torch.uint8, device=d)),
+        lambda: cr.quantize_weight(x, out=(torch.empty((64, 128), dtype=torch.int8, device=d),
+                                           torch.empty((64,), dtype=torch.float32, device=d))),
+        lambda: cr.gemm_i8_i32(qw, qw[:64].contiguous(), 0),                    # fine shapes ...
+    ]
+    for i, fn in enumerate(bad[:-1]):
+        with pytest.raises(ValueError):
+            fn()
+    torch.cuda.synchronize()
+    # ... and a well-formed call still works afterwards
+    acc = bad[-1]()
+    torch.cuda.synchronize()
+    assert tuple(acc.shape) == (128, 64) and int(acc.abs().max().item()) == 0

@@ -108,6 +108,29 @@ def _req(t: torch.Tensor, name: str, dtype, ndim: int):
     return t
 
 
+def _like(t, name: str, dtype, shape):
+    """Check a tensor handed to the kernels: dtype, GPU, contiguous, exact shape."""
+    _req(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _out(t, name: str, dtype, shape, device):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return _like(t, name, dtype, shape)
+
+
+def _ws(t, need: int, device):
+    if t is None:
+        return _workspace(need, device)
+    _req(t, "workspace", torch.uint8, 1)
+    if t.numel() < need:
+        raise ValueError(f"workspace holds {t.numel()} bytes, {need} needed")
+    return t
+
+
 def _call(name: str, *args):
     st = getattr(lib(), name)(*args)
     if st != 0:
@@ -128,9 +151,9 @@ def quantize_weight(w: torch.Tensor, block: int = BLOCK, chunk_rows: int = 0, ou
     """Load-time quantization of a bf16 weight [rows, cols] -> (int8 codes, fp32 scales)."""
     _req(w, "w", torch.bfloat16, 2)
     rows, cols = w.shape
-    q, s = out if out is not None else (
-        torch.empty((rows, cols), dtype=torch.int8, device=w.device),
-        torch.empty((rows,), dtype=torch.float32, device=w.device))
+    q0, s0 = out if out is not None else (None, None)
+    q = _out(q0, "q", torch.int8, (rows, cols), w.device)
+    s = _out(s0, "scale", torch.float32, (rows,), w.device)
     _call("convrot_quantize_weight", _ptr(w), rows, cols, block, chunk_rows, _ptr(q), _ptr(s),
           _stream())
     return q, s
@@ -153,11 +176,12 @@ def linear_fwd(x, qw, sw, bias=None, out=None, workspace=None):
     _req(sw, "sw", torch.float32, 1)
     M, K = x.shape
     N = qw.shape[0]
+    _like(qw, "qw", torch.int8, (N, K))
+    _like(sw, "sw", torch.float32, (N,))
     if bias is not None:
-        _req(bias, "bias", torch.bfloat16, 1)
-    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    need = workspace_bytes(OP_LINEAR_FWD, M, N, K)
-    ws = workspace if workspace is not None else _workspace(need, x.device)
+        _like(bias, "bias", torch.bfloat16, (N,))
+    y = _out(out, "out", torch.bfloat16, (M, N), x.device)
+    ws = _ws(workspace, workspace_bytes(OP_LINEAR_FWD, M, N, K), x.device)
     _call("convrot_linear_fwd", _ptr(x), M, K, _ptr(qw), _ptr(sw), N, _ptr(bias), _ptr(y),
           _ptr(ws), ws.numel(), _stream())
     return y
@@ -165,9 +189,16 @@ def linear_fwd(x, qw, sw, bias=None, out=None, workspace=None):
 
 def gemm_i8_bf16(qx, sx, qw, sw, bias=None, out=None):
     """Second stage of the forward: int8 GEMM + dequantizing epilogue."""
+    _req(qx, "qx", torch.int8, 2)
+    _req(qw, "qw", torch.int8, 2)
     M, K = qx.shape
     N = qw.shape[0]
-    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=qx.device)
+    _like(qw, "qw", torch.int8, (N, K))
+    _like(sx, "sx", torch.float32, (M,))
+    _like(sw, "sw", torch.float32, (N,))
+    if bias is not None:
+        _like(bias, "bias", torch.bfloat16, (N,))
+    y = _out(out, "out", torch.bfloat16, (M, N), qx.device)
     _call("convrot_gemm_i8_bf16", _ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), M, N, K, _ptr(bias),
           _ptr(y), _stream())
     return y
@@ -178,8 +209,13 @@ def gemm_i8_i32(a, b, b_layout: int = 0, out=None):
     _req(a, "a", torch.int8, 2)
     _req(b, "b", torch.int8, 2)
     M, K = a.shape
-    N = b.shape[0] if b_layout == 0 else b.shape[1]
-    acc = out if out is not None else torch.empty((M, N), dtype=torch.int32, device=a.device)
+    if b_layout == 0:
+        N = b.shape[0]
+        _like(b, "b", torch.int8, (N, K))
+    else:
+        N = b.shape[1]
+        _like(b, "b", torch.int8, (K, N))
+    acc = _out(out, "out", torch.int32, (M, N), a.device)
     _call("convrot_gemm_i8_i32", _ptr(a), _ptr(b), M, N, K, b_layout, _ptr(acc), _stream())
     return acc
 
@@ -189,6 +225,7 @@ def bwd_quant_dy(dy, sw):
     _req(dy, "dy", torch.bfloat16, 2)
     _req(sw, "sw", torch.float32, 1)
     M, N = dy.shape
+    _like(sw, "sw", torch.float32, (N,))
     q = torch.empty((M, N), dtype=torch.int8, device=dy.device)
     s = torch.empty((M,), dtype=torch.float32, device=dy.device)
     _call("convrot_bwd_quant_dy", _ptr(dy), M, N, _ptr(sw), _ptr(q), _ptr(s), _stream())
@@ -202,9 +239,10 @@ def linear_bwd_dx(dy, qw, sw, mode: int = BWD_BF16, out=None, workspace=None):
     _req(sw, "sw", torch.float32, 1)
     M, N = dy.shape
     K = qw.shape[1]
-    dx = out if out is not None else torch.empty((M, K), dtype=torch.bfloat16, device=dy.device)
-    need = workspace_bytes(OP_LINEAR_BWD_DX, M, N, K, mode)
-    ws = workspace if workspace is not None else _workspace(need, dy.device)
+    _like(qw, "qw", torch.int8, (N, K))
+    _like(sw, "sw", torch.float32, (N,))
+    dx = _out(out, "out", torch.bfloat16, (M, K), dy.device)
+    ws = _ws(workspace, workspace_bytes(OP_LINEAR_BWD_DX, M, N, K, mode), dy.device)
     _call("convrot_linear_bwd_dx", _ptr(dy), M, N, _ptr(qw), _ptr(sw), K, mode, _ptr(dx),
           _ptr(ws), ws.numel(), _stream())
     return dx
@@ -214,6 +252,7 @@ def dequant_weight_t(qw, sw):
     """Transient bf16 weight of the bf16 input gradient, transposed: [K, N]."""
     _req(qw, "qw", torch.int8, 2)
     N, K = qw.shape
+    _like(sw, "sw", torch.float32, (N,))
     out = torch.empty((K, N), dtype=torch.bfloat16, device=qw.device)
     _call("convrot_dequant_weight_t", _ptr(qw), _ptr(sw), N, K, _ptr(out), _stream())
     return out
@@ -226,7 +265,10 @@ def embedding_lookup(ids, qe, se, oob_count=None, out=None):
     _req(se, "se", torch.float32, 1)
     T = ids.shape[0]
     V, D = qe.shape
-    o = out if out is not None else torch.empty((T, D), dtype=torch.bfloat16, device=qe.device)
+    _like(se, "se", torch.float32, (V,))
+    if oob_count is not None:
+        _like(oob_count, "oob_count", torch.int32, (1,))
+    o = _out(out, "out", torch.bfloat16, (T, D), qe.device)
     _call("convrot_embedding_lookup", _ptr(ids), T, _ptr(qe), _ptr(se), V, D, _ptr(o),
           _ptr(oob_count), _stream())
     return o

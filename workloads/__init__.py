@@ -180,6 +180,12 @@ def packed_weight(layer: int, base: int = 0, N: int = 4096, K: int = 4096) -> np
     return out
 
 
+def qkv_weights(base: int = 0, N: int = 4096, K: int = 4096) -> list:
+    """The q, k and v projection weights that share one input (their own seed
+    streams, disjoint from the streamed layers')."""
+    return [packed_weight(1000 + j, base, N, K) for j in range(3)]
+
+
 EMBED_V, EMBED_D, EMBED_CHUNK, EMBED_T = 248320, 4096, 8192, 32768
 
 
