@@ -1,0 +1,272 @@
+// Span quantizer: the device-side rotate (or scale-fold) + per-row int8
+// quantization of up to 32 consecutive 128-blocks held in LDS.  Shared by the
+// standalone quantizer kernels and the single-launch forward.
+//
+// Arithmetic (bit-exact by construction):
+//   rotate:   per 128-block, S_j = sum_i H[i][j] x_i computed by a fast
+//             Walsh-Hadamard transform in binary64.  bf16 inputs make every
+//             partial sum exact (a block's magnitude spread would have to exceed
+//             2^38 before binary64 rounds), so the butterfly order cannot change
+//             the result; r_j = fl32(fl64(S_j * c)), c = 1/sqrt(128).
+//   fold:     (dY quantizer) r_n = fl32(fl32(dY_n) * s_w[n]); no rotation.
+//   quantize: a = max|r|, s = fl32(a/127), code = RNE(fl32(r/s)); all-zero row
+//             -> s = 0, codes 0.
+//
+// Work layout.  A wave owns a span of up to 32 consecutive 128-blocks (4096
+// elements): one row of K = 4096, several short rows packed together, or a
+// 4096-wide slice of a long row (then the workgroup's waves share the row and
+// combine their maxima through LDS).  The span is copied to LDS with direct
+// 16-byte global->LDS loads (coalesced, XOR-swizzled so the transposed reads
+// are bank-conflict free) and processed in two passes of 16 blocks: in pass k
+// lane 16 g + p holds elements 32 g .. 32 g + 31 of block 16 k + p.  Five
+// butterfly stages run inside the lane, the sixth pairs lane L with L + 16
+// (v_permlane16_swap) and the seventh with L + 32 (v_permlane32_swap).  With
+// 32 values per lane a wave needs ~150 VGPRs, so three waves share a SIMD and
+// cover each other's load latency.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace convrot {
+namespace {
+
+constexpr int kSpanBlocks = 32;                  // blocks per wave span
+constexpr int kSpanBytes = kSpanBlocks * 256;    // bf16 bytes per wave span
+
+enum Mode { kRotate = 0, kFold = 1 };
+
+// LDS position (in 16-byte units) of chunk c (0..15) of block b.
+__device__ __forceinline__ int lds_chunk(int b, int c) { return (b << 4) | (c ^ (b & 7)); }
+
+// Exchange with the neighbouring 16-lane row: rows 1 and 3 of vdst swap with
+// rows 0 and 2 of src0 (v_permlane16_swap).
+__device__ __forceinline__ void swap_rows16(double& vdst, double& src0) {
+  uint64_t a = __builtin_bit_cast(uint64_t, vdst), b = __builtin_bit_cast(uint64_t, src0);
+  auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)a, (uint32_t)b, false, false);
+  auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(a >> 32), (uint32_t)(b >> 32), false, false);
+  vdst = __builtin_bit_cast(double, ((uint64_t)hi[0] << 32) | lo[0]);
+  src0 = __builtin_bit_cast(double, ((uint64_t)hi[1] << 32) | lo[1]);
+}
+
+// Quantize one staged span: per pass read the lane's 32 values from LDS and
+// rotate them (or fold the column scale); then reduce the row maxima,
+// quantize, stage the codes in LDS and store them.
+//
+// Rotation data flow: the in-lane stages cover element bits 0-4 (register
+// index e).  Each cross-lane swap pairs v[e] with v[e + 16] and exchanges
+// register bit 4 with a lane bit, so that the butterfly partners meet in one
+// lane.  After both, lane quarter q = L >> 4 holds outputs 16 q + e in v[e]
+// and 64 + 16 q + e in v[e + 16] (e < 16).
+template <int MODE>
+__device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_blocks, int nb,
+                                              int64_t span_elem0, int blk_in_row0, int64_t row0,
+                                              int waves_per_row, int8_t* __restrict__ q,
+                                              float* __restrict__ scale,
+                                              const float* __restrict__ colscale,
+                                              float* seg_max_wave, float* row_part_max) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int p = lane & 15;   // block within the pass
+  const int g = lane >> 4;   // which quarter of the block
+
+  float r[2][32];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    // keep the two passes apart: interleaving them would hold both passes'
+    // binary64 working sets at once
+    __builtin_amdgcn_sched_barrier(0);
+    const int b = 16 * k + p;
+    const bool active = b < span_blocks;
+    if (k == 1 && span_blocks <= 16) {  // wave-uniform: the span fits in one pass
+#pragma unroll
+      for (int e = 0; e < 32; ++e) r[1][e] = 0.f;
+      continue;
+    }
+    uint4 raw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      raw[i] = *reinterpret_cast<const uint4*>(my_lds + 16 * lds_chunk(b, 4 * g + i));
+    if (MODE == kRotate) {
+      double v[32];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * i + 2 * j] = (double)bf16lo_to_f32(w[j]);
+          v[8 * i + 2 * j + 1] = (double)bf16hi_to_f32(w[j]);
+        }
+      }
+      if (!active) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) v[e] = 0.0;
+      }
+#pragma unroll
+      for (int bit = 1; bit < 32; bit <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          if (e & bit) continue;
+          double a = v[e], c = v[e | bit];
+          v[e] = a + c;
+          v[e | bit] = a - c;
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one stage at a time (register pressure)
+      }
+      // element bit 5: lane L with L + 16
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        swap_rows16(v[e], v[e + 16]);
+        double a = v[e], c = v[e + 16];
+        v[e] = a + c;
+        v[e + 16] = a - c;
+      }
+      // element bit 6: lane L with L + 32
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        swap_halves(v[e], v[e + 16]);
+        double a = v[e], c = v[e + 16];
+        v[e] = a + c;
+        v[e + 16] = a - c;
+      }
+#pragma unroll
+      for (int e = 0; e < 32; ++e) r[k][e] = (float)(v[e] * kInvSqrt128);
+    } else {
+      // fold the per-column scale: element 32 g + e of block b
+      const int64_t col0 =
+          active ? (int64_t)(blk_in_row0 + (waves_per_row == 1 ? b % nb : b)) * kBlock + 32 * g
+                 : 0;
+      const float4* cs = reinterpret_cast<const float4*>(colscale + col0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+        float4 s0 = active ? cs[2 * i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 s1 = active ? cs[2 * i + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+        float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          r[k][8 * i + 2 * j] = bf16lo_to_f32(w[j]) * sc[2 * j];
+          r[k][8 * i + 2 * j + 1] = bf16hi_to_f32(w[j]) * sc[2 * j + 1];
+        }
+      }
+      if (!active) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) r[k][e] = 0.f;
+      }
+    }
+  }
+
+  // ---- row absmax ------------------------------------------------------------
+  float m[2] = {0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) m[k] = fmaxf(m[k], fabsf(r[k][e]));
+    m[k] = fmaxf(m[k], __shfl_xor(m[k], 16, kWave));  // the four quarters of the block
+    m[k] = fmaxf(m[k], __shfl_xor(m[k], 32, kWave));
+  }
+  if (waves_per_row == 1) {
+    if (nb == 32) {
+      const float mm = wave_max_xor(fmaxf(m[0], m[1]), 16);
+      m[0] = m[1] = mm;
+    } else if ((nb & (nb - 1)) == 0) {
+      m[0] = wave_max_xor(m[0], nb);       // aligned segments of nb blocks
+      m[1] = wave_max_xor(m[1], nb);
+    } else {
+      if (g == 0) {
+        seg_max_wave[p] = m[0];
+        seg_max_wave[16 + p] = m[1];
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int first = ((16 * k + p) / nb) * nb;
+        float mm = 0.f;
+        for (int j = 0; j < nb; ++j) {
+          const int idx = first + j;
+          if (idx < kSpanBlocks) mm = fmaxf(mm, seg_max_wave[idx]);
+        }
+        m[k] = mm;
+      }
+    }
+  } else {
+    const float mw = wave_max_xor(fmaxf(m[0], m[1]), 16);
+    if (lane == 0) row_part_max[wave] = mw;
+    __syncthreads();
+    float mm = 0.f;
+    for (int w = 0; w < waves_per_row; ++w) mm = fmaxf(mm, row_part_max[w]);
+    m[0] = m[1] = mm;
+  }
+
+  // ---- quantize + stage + store -------------------------------------------------
+  // Codes are staged in LDS (the span's own input buffer, already read) and
+  // stored as whole 1 KB runs: lane i of step j writes 16-byte chunk 64 j + i.
+  // Chunk c of block c/8 sits at c ^ (c/8 & 7) (conflict-free writes).
+  uint8_t* stg = const_cast<uint8_t*>(my_lds);
+  auto phys = [](int c) { return c ^ ((c >> 3) & 7); };
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int b = 16 * k + p;
+    const float s = m[k] / 127.0f;                     // IEEE binary32 division
+    const bool fast = s > 0x1p-100f && s < 0x1p100f;
+    const float inv = s > 0.f ? 1.0f / s : 0.f;        // RN(1/s)
+    // Quotients: the 3-operation correctly rounded form when every lane's row
+    // scale is in range (wave-uniform branch), else the IEEE division per lane.
+    float t[32];
+    if (__builtin_amdgcn_ballot_w64(!fast) == 0) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) t[e] = quot_rn(r[k][e], s, inv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) t[e] = fast ? quot_rn(r[k][e], s, inv) : (s > 0.f ? r[k][e] / s : 0.f);
+    }
+    uint32_t packed[8];
+#pragma unroll
+    for (int gg = 0; gg < 8; ++gg) {
+      packed[gg] = pack_low_bytes(rne_low_byte_bits(t[4 * gg]), rne_low_byte_bits(t[4 * gg + 1]),
+                                  rne_low_byte_bits(t[4 * gg + 2]), rne_low_byte_bits(t[4 * gg + 3]));
+    }
+    if (b < span_blocks) {
+      const int c_lo = 8 * b + (MODE == kRotate ? g : 2 * g);
+      const int c_hi = 8 * b + (MODE == kRotate ? 4 + g : 2 * g + 1);
+      *reinterpret_cast<uint4*>(stg + 16 * phys(c_lo)) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      *reinterpret_cast<uint4*>(stg + 16 * phys(c_hi)) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+      if (waves_per_row == 1 && g == 0 && b % nb == 0) scale[row0 + b / nb] = s;
+    }
+    if (k == 0 && waves_per_row > 1 && wave == 0 && lane == 0) scale[row0] = s;
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staging writes landed
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+  const int nchunks = span_blocks * 8;
+  int8_t* dst = q + span_elem0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = 64 * j + lane;
+    if (c < nchunks)
+      *reinterpret_cast<uint4*>(dst + 16 * c) = *reinterpret_cast<const uint4*>(stg + 16 * phys(c));
+  }
+}
+
+// Issue the 8 direct-to-LDS loads of a span of span_blocks (>= 1) blocks.
+// Slots past the span reload its last chunk so every lane always issues the
+// same number of loads (the vmcnt bookkeeping relies on it).
+__device__ __forceinline__ void stage_span(const uint16_t* __restrict__ x, int64_t span_elem0,
+                                           int span_blocks, uint8_t* my_lds) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_u32(my_lds));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int slot = i * 64 + lane;
+    int b = slot >> 4;
+    int c = (slot & 15) ^ (b & 7);
+    if (b >= span_blocks) { b = span_blocks - 1; c = 15; }
+    dma16(x + span_elem0 + (int64_t)b * kBlock + c * 8, base + i * 1024);
+  }
+}
+
+}  // namespace
+}  // namespace convrot
+
