@@ -47,6 +47,8 @@ def lib():
         L.oracle_dequant_weight.argtypes = [p, p, i64, i64, i32, p]
         L.oracle_bf16_gemm_dx.argtypes = [p, p, i64, i64, i64, p, i64, p]
         L.oracle_embedding_lookup.argtypes = [p, i64, p, p, i64, i64, i32, p, p]
+        L.oracle_lora_down.argtypes = [p, i64, i64, p, i64, p, i64, p]
+        L.oracle_lora_epilogue.argtypes = [p, i64, i64, p, p, p, p, p, p, i64, C.c_double, p]
         L.oracle_double_to_bf16.argtypes = [C.c_double]
         L.oracle_double_to_bf16.restype = C.c_uint16
         L.oracle_rne_integer.argtypes = [C.c_double]
@@ -180,6 +182,44 @@ def linear_fwd(x_bf16, qw, sw, bias=None, rows=None, block: int = BLOCK):
     acc = gemm_i8_i32(qx, qw, rows)
     y = dequant_epilogue(acc, sx, sw, rows, bias)
     return dict(qx=qx, sx=sx, acc=acc, y=y, inexact_rows=bad)
+
+
+# --------------------------------------------------------------------------
+# O13: LoRA branch of the forward
+# --------------------------------------------------------------------------
+
+def lora_down(x_bf16, a_bf16, rows=None) -> np.ndarray:
+    """xa = bf16(x . A^T) (binary64 sum) for the listed rows of x; A is [R, K]."""
+    x = _c(x_bf16, np.uint16)
+    a = _c(a_bf16, np.uint16)
+    M, K = x.shape
+    R, Ka = a.shape
+    assert Ka == K
+    r = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    nr = M if r is None else r.size
+    xa = np.empty((nr, R), dtype=np.uint16)
+    _check(lib().oracle_lora_down(_ptr(x), M, K, _ptr(a), R, _ptr(r), nr, _ptr(xa)), "lora_down")
+    return xa
+
+
+def lora_epilogue(acc, sx, sw, xa, b_bf16, scale: float, rows=None, bias=None) -> np.ndarray:
+    """y = bf16(acc*s_x*s_w + bias + scale * xa . B^T), binary64, one rounding."""
+    acc = _c(acc, np.int32)
+    sx = _c(sx, np.float32)
+    sw = _c(sw, np.float32)
+    xa = _c(xa, np.uint16)
+    b = _c(b_bf16, np.uint16)
+    nr, N = acc.shape
+    R = xa.shape[1]
+    assert b.shape == (N, R) and xa.shape[0] == nr
+    r = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    if bias is not None:
+        bias = _c(bias, np.uint16)
+    y = np.empty((nr, N), dtype=np.uint16)
+    _check(lib().oracle_lora_epilogue(_ptr(acc), nr, N, _ptr(sx), _ptr(r), _ptr(sw), _ptr(bias),
+                                      _ptr(xa), _ptr(b), R, C.c_double(scale), _ptr(y)),
+           "lora_epilogue")
+    return y
 
 
 # --------------------------------------------------------------------------

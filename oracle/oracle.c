@@ -444,6 +444,56 @@ int oracle_embedding_lookup(const int32_t* ids, int64_t T, const int8_t* qe, con
     return ORACLE_OK;
 }
 
+/* ------------------------------------------------------------------ */
+/* O13: LoRA branch of the forward ([G71]: the quantized layers stay    */
+/* LoRA-trainable and the LoRA branch receives the unrotated input)     */
+/* ------------------------------------------------------------------ */
+
+/* Down projection, as a bf16 Linear: xa[i][r] = bf16( sum_k x[m][k] * A[r][k] )
+ * for the listed rows m = rows[i] (rows == NULL: all M rows), the sum taken in
+ * index order in binary64.  A is [R, K]. */
+int oracle_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint16_t* A, int64_t R,
+                     const int64_t* rows, int64_t nrows, uint16_t* xa) {
+    if (!x || !A || !xa || M < 0 || K <= 0 || R <= 0) return ORACLE_EINVAL;
+    if (!rows) nrows = M;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t m = rows ? rows[i] : i;
+        for (int64_t r = 0; r < R; ++r) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                s += bf16_to_double(x[m * K + k]) * bf16_to_double(A[r * K + k]);
+            xa[i * R + r] = double_to_bf16(s);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Forward output with the LoRA branch:
+ *   y[i][n] = bf16( acc[i][n] * s_x[m] * s_w[n] + bias[n]
+ *                   + scale * sum_r xa[i][r] * B[n][r] ),   m = rows[i],
+ * evaluated in binary64 and rounded once.  B is [N, R]; bias may be NULL. */
+int oracle_lora_epilogue(const int32_t* acc, int64_t nrows, int64_t N, const float* sx,
+                         const int64_t* rows, const float* sw, const uint16_t* bias,
+                         const uint16_t* xa, const uint16_t* B, int64_t R, double scale,
+                         uint16_t* y) {
+    if (!acc || !sx || !sw || !xa || !B || !y || nrows < 0 || N < 0 || R <= 0)
+        return ORACLE_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t m = rows ? rows[i] : i;
+        for (int64_t n = 0; n < N; ++n) {
+            double l = 0.0;
+            for (int64_t r = 0; r < R; ++r)
+                l += bf16_to_double(xa[i * R + r]) * bf16_to_double(B[n * R + r]);
+            double v = (double)acc[i * N + n] * (double)sx[m] * (double)sw[n];
+            if (bias) v = v + bf16_to_double(bias[n]);
+            y[i * N + n] = double_to_bf16(v + scale * l);
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* Threads the OpenMP loops above use (reported with oracle timings). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 

@@ -420,3 +420,84 @@ def test_oracle_regression_digests(oracle_mod):
     with open(os.path.join(here, "tiny_oracle_digests.json")) as f:
         stored = json.load(f)
     assert make_golden.digests() == stored
+
+
+# --------------------------------------------------------------------------
+# O13: LoRA branch (down projection to bf16, up projection in the epilogue)
+# --------------------------------------------------------------------------
+
+def _bf16(vals):
+    return wl.f32_to_bf16_bits(np.asarray(vals, dtype=np.float32))
+
+
+def test_lora_down_worked_example(oracle_mod):
+    # x = [1, 2], A = [[3, 4], [-0.5, 0.25]]: xa = [1*3 + 2*4, -0.5 + 0.5] = [11, 0]
+    x = _bf16([[1.0, 2.0]])
+    a = _bf16([[3.0, 4.0], [-0.5, 0.25]])
+    xa = oracle_mod.lora_down(x, a)
+    assert xa.tolist() == _bf16([[11.0, 0.0]]).tolist()
+
+
+def test_lora_down_rounds_once_to_bf16(oracle_mod):
+    # bf16 spacing above 1 is 2^-7: 1 + 2^-8 is the midpoint (tie -> even, 1.0),
+    # 1 + 3*2^-9 lies above it (-> 1 + 2^-7); both sums are exact in binary64
+    x = _bf16([[1.0, 1.0]])
+    a = _bf16([[1.0, 2.0 ** -8], [1.0, 3 * 2.0 ** -9]])
+    xa = oracle_mod.lora_down(x, a)
+    assert xa[0].tolist() == _bf16([1.0, 1.0 + 2.0 ** -7]).tolist()
+
+
+def test_lora_down_one_hot_is_identity(oracle_mod):
+    g = np.random.default_rng(3)
+    K, R = 256, 16
+    x = _bf16(g.standard_normal((5, K)))
+    a = np.zeros((R, K), dtype=np.uint16)
+    a[np.arange(R), 7 * np.arange(R)] = _bf16([1.0])[0]
+    xa = oracle_mod.lora_down(x, a)
+    assert np.array_equal(xa, x[:, 7 * np.arange(R)])
+    # rows subset
+    xa2 = oracle_mod.lora_down(x, a, rows=[4, 1])
+    assert np.array_equal(xa2, xa[[4, 1]])
+
+
+def test_lora_epilogue_zero_branch_is_base(oracle_mod):
+    g = np.random.default_rng(4)
+    acc = g.integers(-30000, 30000, (3, 8), dtype=np.int32)
+    sx = (g.random(3) + 0.1).astype(np.float32) * 1e-3
+    sw = (g.random(8) + 0.1).astype(np.float32) * 1e-3
+    bias = _bf16(g.standard_normal(8))
+    xa = _bf16(g.standard_normal((3, 16)))
+    base = oracle_mod.dequant_epilogue(acc, sx, sw, bias=bias)
+    zero_b = np.zeros((8, 16), dtype=np.uint16)
+    assert np.array_equal(oracle_mod.lora_epilogue(acc, sx, sw, xa, zero_b, 0.75, bias=bias), base)
+    b = _bf16(g.standard_normal((8, 16)))
+    assert np.array_equal(oracle_mod.lora_epilogue(acc, sx, sw, xa, b, 0.0, bias=bias), base)
+
+
+def test_lora_epilogue_worked_example(oracle_mod):
+    # acc = 0: y = bf16(scale * sum_r xa_r * B_nr); xa = [2, -1], B = [[0.5, 1], [3, 0]]
+    acc = np.zeros((1, 2), dtype=np.int32)
+    sx = np.ones(1, dtype=np.float32)
+    sw = np.ones(2, dtype=np.float32)
+    xa = _bf16([[2.0, -1.0]])
+    b = _bf16([[0.5, 1.0], [3.0, 0.0]])
+    y = oracle_mod.lora_epilogue(acc, sx, sw, xa, b, 0.25)
+    assert y.tolist() == _bf16([[0.0, 1.5]]).tolist()
+    # with a base term: acc 100 * 0.5 * 0.25 = 12.5, plus 0.25 * [0, 6]
+    acc2 = np.full((1, 2), 100, dtype=np.int32)
+    y2 = oracle_mod.lora_epilogue(acc2, np.array([0.5], np.float32), np.array([0.25, 0.25], np.float32),
+                                  xa, b, 0.25)
+    assert y2.tolist() == _bf16([[12.5, 14.0]]).tolist()
+
+
+def test_lora_epilogue_scale_power_of_two_invariance(oracle_mod):
+    # scale * B == (2 scale) * (B / 2) exactly when B / 2 stays a normal bf16
+    g = np.random.default_rng(5)
+    acc = g.integers(-30000, 30000, (4, 6), dtype=np.int32)
+    sx = (g.random(4) + 0.1).astype(np.float32) * 1e-3
+    sw = (g.random(6) + 0.1).astype(np.float32) * 1e-3
+    xa = _bf16(g.standard_normal((4, 32)))
+    bf = wl.bf16_bits_to_f32(_bf16(g.standard_normal((6, 32))))
+    y1 = oracle_mod.lora_epilogue(acc, sx, sw, xa, _bf16(bf), 0.375)
+    y2 = oracle_mod.lora_epilogue(acc, sx, sw, xa, _bf16(bf / 2), 0.75)
+    assert np.array_equal(y1, y2)
