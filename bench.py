@@ -179,6 +179,18 @@ def main():
     }
     wq_ms = time_ms(lambda: cr.quantize_weight(w, out=(qw, sw)), 3, 20)
     extra["weight_quant_attn_us"] = round(wq_ms * 1e3, 2)
+    # the same forward with a rank-16 LoRA branch on the unrotated input
+    lw = wl.lora_weights(K, N, 16, 0)
+    la, lb = to_dev(lw["a"]), to_dev(lw["b"])
+    ws_l = torch.empty(cr.workspace_bytes(cr.OP_LINEAR_FWD_LORA, M, N, K, 16), dtype=torch.uint8,
+                       device=dev)
+    lora_ms = time_ms(lambda: cr.linear_fwd_lora(x, qw, sw, la, lb, 1.0, out=y, workspace=ws_l), 10, 200)
+    ld_ms = time_ms(lambda: cr.lora_down(x, la), 10, 200)
+    extra["lora16_fwd_us"] = round(lora_ms * 1e3, 2)
+    extra["lora16_fwd_tops"] = round(ops / (lora_ms * 1e-3) / 1e12, 1)
+    extra["lora16_down_us"] = round(ld_ms * 1e3, 2)
+    log(f"[bench] with a rank-16 LoRA branch: {lora_ms * 1e3:.1f} us/call "
+        f"(down projection alone {ld_ms * 1e3:.1f} us)")
     del x, w, ws, y, y2, qx, sx
 
     if args.only == "all":

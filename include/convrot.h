@@ -58,6 +58,7 @@ extern "C" {
 /* Operations for convrot_workspace_bytes. */
 #define CONVROT_OP_LINEAR_FWD 0
 #define CONVROT_OP_LINEAR_BWD_DX 1
+#define CONVROT_OP_LINEAR_FWD_LORA 2  /* mode = LoRA rank */
 
 /* Largest supported contraction length of the row quantizer (32768 = 256 blocks). */
 #define CONVROT_MAX_ROW_LEN 32768
@@ -93,6 +94,26 @@ int convrot_quantize_weight(const uint16_t* w, int64_t rows, int64_t cols, int32
 int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw,
                        const float* sw, int64_t N, const uint16_t* bias, uint16_t* y,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Forward with a LoRA branch.  The quantized layers stay LoRA-trainable and the
+ * LoRA branch receives the unrotated input (training guide section 7.1, ConvRot
+ * INT8 scope bullet):
+ *   xa = bf16( x * A^T )                       (as a bf16 Linear; fp32 accumulation)
+ *   y  = bf16( fl32(acc) * s_x[m] * s_w[n] (+ bias[n]) + lora_scale * (xa[m] . B[n]) )
+ * with the base terms exactly as in convrot_linear_fwd and the LoRA term added in
+ * fp32 before the single bf16 rounding.
+ *   lora_a  bf16 [R, K] (down projection);  lora_b bf16 [N, R] (up projection)
+ *   R       16 or 32 (otherwise CONVROT_ESHAPE)
+ *   lora_scale  multiplier * alpha / R, applied to the up projection
+ *   workspace  >= convrot_workspace_bytes(CONVROT_OP_LINEAR_FWD_LORA, M, N, K, R)
+ * Other arguments, errors and ownership as convrot_linear_fwd.
+ */
+int convrot_linear_fwd_lora(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw,
+                            const float* sw, int64_t N, const uint16_t* bias,
+                            const uint16_t* lora_a, const uint16_t* lora_b, int32_t R,
+                            float lora_scale, uint16_t* y, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Input gradient of the frozen base (the pull request's utils bullet: only
@@ -160,6 +181,11 @@ int convrot_bwd_quant_dy(const uint16_t* dy, int64_t M, int64_t N, const float* 
  * transpose of W_hat = bf16( (s_w * q_w) * R ). */
 int convrot_dequant_weight_t(const int8_t* qw, const float* sw, int64_t N, int64_t K,
                              uint16_t* what_t, hipStream_t stream);
+
+/* First stage of the LoRA forward: xa [M, R] bf16 = bf16( x [M, K] * lora_a [R, K]^T )
+ * with fp32 accumulation.  R 16 or 32, K % 128 == 0. */
+int convrot_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint16_t* lora_a,
+                      int32_t R, uint16_t* xa, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -55,6 +55,10 @@ def test_workspace_sizes(cr):
     assert cr.workspace_bytes(cr.OP_LINEAR_BWD_DX, M, N, K, cr.BWD_BF16) == 2 * N * K
     assert cr.workspace_bytes(cr.OP_LINEAR_FWD, 0, N, K) == 0
     assert cr.workspace_bytes(9, M, N, K) == 0
+    # LoRA forward: the forward's q_x / s_x plus xa [M, R] bf16; R in {16, 32}
+    for R in (16, 32):
+        assert cr.workspace_bytes(cr.OP_LINEAR_FWD_LORA, M, N, K, R) == M * K + 4 * M + 2 * M * R
+    assert cr.workspace_bytes(cr.OP_LINEAR_FWD_LORA, M, N, K, 8) == 0
 
 
 # Fake, well-aligned, never-dereferenced device addresses: validation must reject
@@ -71,6 +75,8 @@ def test_null_pointers_are_einval(cr):
     assert L.convrot_quantize_weight(None, 4, 128, 128, 0, B, Y, None) == -1
     assert L.convrot_embedding_lookup(None, 4, B, B, 10, 128, Y, None, None) == -1
     assert L.convrot_linear_bwd_dx(A, 4, 128, None, B, 128, 0, Y, WS, 1 << 20, None) == -1
+    assert L.convrot_linear_fwd_lora(A, 4, 128, B, B, 4, None, None, B, 16, 1.0, Y, WS, 1 << 20,
+                                     None) == -1
 
 
 def test_bad_sizes_and_shapes(cr):
@@ -85,6 +91,11 @@ def test_bad_sizes_and_shapes(cr):
     assert L.convrot_linear_bwd_dx(A, 4, 128, B, B, 128, 2, Y, WS, 1 << 20, None) == -1
     assert L.convrot_gemm_i8_i32(A, B, 4, 100, 128, 1, Y, None) == -2
     assert L.convrot_gemm_i8_i32(A, B, 4, 100, 128, 3, Y, None) == -1
+    # LoRA rank must be 16 or 32; the workspace must hold q_x, s_x and xa
+    assert L.convrot_linear_fwd_lora(A, 4, 128, B, B, 4, None, A, B, 8, 1.0, Y, WS, 1 << 20,
+                                     None) == -2
+    assert L.convrot_linear_fwd_lora(A, 4, 128, B, B, 4, None, A, B, 16, 1.0, Y, WS, 512,
+                                     None) == -3
 
 
 def test_misalignment_is_einval(cr):

@@ -19,7 +19,7 @@ __all__ = [
     "BLOCK", "BWD_BF16", "BWD_INT8", "ConvRotError", "lib", "library_path",
     "quantize_weight", "quantize_act", "linear_fwd", "gemm_i8_bf16", "gemm_i8_i32",
     "bwd_quant_dy", "linear_bwd_dx", "dequant_weight_t", "embedding_lookup",
-    "workspace_bytes", "EXPORTS",
+    "workspace_bytes", "linear_fwd_lora", "lora_down", "EXPORTS",
 ]
 
 BLOCK = 128
@@ -27,6 +27,7 @@ BWD_BF16 = 0
 BWD_INT8 = 1
 OP_LINEAR_FWD = 0
 OP_LINEAR_BWD_DX = 1
+OP_LINEAR_FWD_LORA = 2  # mode = LoRA rank
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libconvrot.so")
@@ -36,7 +37,8 @@ EXPORTS = (
     "convrot_quantize_weight", "convrot_linear_fwd", "convrot_linear_bwd_dx",
     "convrot_embedding_lookup", "convrot_workspace_bytes", "convrot_status_string",
     "convrot_quantize_act", "convrot_gemm_i8_bf16", "convrot_gemm_i8_i32",
-    "convrot_bwd_quant_dy", "convrot_dequant_weight_t",
+    "convrot_bwd_quant_dy", "convrot_dequant_weight_t", "convrot_linear_fwd_lora",
+    "convrot_lora_down",
 )
 
 
@@ -71,6 +73,9 @@ def lib():
             "convrot_gemm_i8_i32": [p, p, i64, i64, i64, i32, p, p],
             "convrot_bwd_quant_dy": [p, i64, i64, p, p, p, p],
             "convrot_dequant_weight_t": [p, p, i64, i64, p, p],
+            "convrot_linear_fwd_lora": [p, i64, i64, p, p, i64, p, p, p, i32, C.c_float, p, p,
+                                        sz, p],
+            "convrot_lora_down": [p, i64, i64, p, i32, p, p],
         }
         for name, argt in sig.items():
             f = getattr(L, name)
@@ -185,6 +190,43 @@ def linear_fwd(x, qw, sw, bias=None, out=None, workspace=None):
     _call("convrot_linear_fwd", _ptr(x), M, K, _ptr(qw), _ptr(sw), N, _ptr(bias), _ptr(y),
           _ptr(ws), ws.numel(), _stream())
     return y
+
+
+def linear_fwd_lora(x, qw, sw, lora_a, lora_b, lora_scale: float, bias=None, out=None,
+                    workspace=None):
+    """ConvRot-int8 linear plus a LoRA branch on the unrotated input:
+    y = linear_fwd(x) + lora_scale * bf16(x . lora_a^T) . lora_b^T, one bf16 rounding.
+    lora_a bf16 [R, K], lora_b bf16 [N, R], R in {16, 32}."""
+    _req(x, "x", torch.bfloat16, 2)
+    _req(qw, "qw", torch.int8, 2)
+    _req(lora_a, "lora_a", torch.bfloat16, 2)
+    M, K = x.shape
+    N = qw.shape[0]
+    R = lora_a.shape[0]
+    _like(qw, "qw", torch.int8, (N, K))
+    _like(sw, "sw", torch.float32, (N,))
+    _like(lora_a, "lora_a", torch.bfloat16, (R, K))
+    _like(lora_b, "lora_b", torch.bfloat16, (N, R))
+    if bias is not None:
+        _like(bias, "bias", torch.bfloat16, (N,))
+    y = _out(out, "out", torch.bfloat16, (M, N), x.device)
+    ws = _ws(workspace, workspace_bytes(OP_LINEAR_FWD_LORA, M, N, K, R), x.device)
+    _call("convrot_linear_fwd_lora", _ptr(x), M, K, _ptr(qw), _ptr(sw), N, _ptr(bias),
+          _ptr(lora_a), _ptr(lora_b), R, float(lora_scale), _ptr(y), _ptr(ws), ws.numel(),
+          _stream())
+    return y
+
+
+def lora_down(x, lora_a):
+    """First stage of the LoRA forward: xa = bf16(x . lora_a^T) [M, R]."""
+    _req(x, "x", torch.bfloat16, 2)
+    _req(lora_a, "lora_a", torch.bfloat16, 2)
+    M, K = x.shape
+    R = lora_a.shape[0]
+    _like(lora_a, "lora_a", torch.bfloat16, (R, K))
+    xa = torch.empty((M, R), dtype=torch.bfloat16, device=x.device)
+    _call("convrot_lora_down", _ptr(x), M, K, _ptr(lora_a), R, _ptr(xa), _stream())
+    return xa
 
 
 def gemm_i8_bf16(qx, sx, qw, sw, bias=None, out=None):

@@ -82,6 +82,8 @@ const char* convrot_status_string(int status) {
 size_t convrot_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t mode) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   if (op == CONVROT_OP_LINEAR_FWD) return fwd_workspace(M, K);
+  if (op == CONVROT_OP_LINEAR_FWD_LORA)
+    return (mode == 16 || mode == 32) ? fwd_workspace(M, K) + align256(2 * (size_t)M * mode) : 0;
   if (op == CONVROT_OP_LINEAR_BWD_DX) {
     if (mode == CONVROT_BWD_INT8) return bwd_int8_workspace(M, N);
     if (mode == CONVROT_BWD_BF16) return bwd_bf16_workspace(N, K);
@@ -138,6 +140,45 @@ int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw
   a.P = qw; a.Q = qx; a.I = N; a.J = M; a.Kc = K; a.ldp = K; a.ldq = K;
   a.out = y; a.ldo = N; a.si = sw; a.sj = sx; a.bias = bias;
   return hip_status(launch_gemm_i8(a, kEpiDequantBf16, false, stream));
+}
+
+int convrot_linear_fwd_lora(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw,
+                            const float* sw, int64_t N, const uint16_t* bias,
+                            const uint16_t* lora_a, const uint16_t* lora_b, int32_t R,
+                            float lora_scale, uint16_t* y, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (!x || !qw || !sw || !y || !lora_a || !lora_b || !workspace || M <= 0 || N <= 0 || K <= 0)
+    return CONVROT_EINVAL;
+  if (!aligned16(x) || !aligned16(qw) || !aligned16(y) || !aligned16(lora_a) ||
+      !aligned16(lora_b) || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return CONVROT_EINVAL;
+  if (!row_len_ok(K) || (R != 16 && R != 32)) return CONVROT_ESHAPE;
+  const size_t xa_off = fwd_workspace(M, K);
+  if (workspace_bytes < xa_off + align256(2 * (size_t)M * R)) return CONVROT_EWORKSPACE;
+  int st = check_device();
+  if (st) return st;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int8_t* qx = reinterpret_cast<int8_t*>(ws);
+  float* sx = reinterpret_cast<float*>(ws + align256((size_t)M * K));
+  uint16_t* xa = reinterpret_cast<uint16_t*>(ws + xa_off);
+  hipError_t e = launch_rotate_quant(x, M, (int)K, qx, sx, nullptr, false, stream);
+  if (e == hipSuccess) e = launch_lora_down(x, M, K, lora_a, R, xa, stream);
+  if (e != hipSuccess) return CONVROT_EHIP;
+  GemmArgs a{};
+  a.P = qw; a.Q = qx; a.I = N; a.J = M; a.Kc = K; a.ldp = K; a.ldq = K;
+  a.out = y; a.ldo = N; a.si = sw; a.sj = sx; a.bias = bias;
+  a.lora_b = lora_b; a.lora_xa = xa; a.lora_r = R; a.lora_scale = lora_scale;
+  return hip_status(launch_gemm_i8(a, kEpiDequantLoraBf16, false, stream));
+}
+
+int convrot_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint16_t* lora_a,
+                      int32_t R, uint16_t* xa, hipStream_t stream) {
+  if (!x || !lora_a || !xa || M <= 0 || K <= 0) return CONVROT_EINVAL;
+  if (!aligned16(x) || !aligned16(lora_a)) return CONVROT_EINVAL;
+  if (!row_len_ok(K) || (R != 16 && R != 32)) return CONVROT_ESHAPE;
+  int st = check_device();
+  if (st) return st;
+  return hip_status(launch_lora_down(x, M, K, lora_a, R, xa, stream));
 }
 
 int convrot_gemm_i8_i32(const int8_t* a_, const int8_t* b, int64_t M, int64_t N, int64_t K,

@@ -227,6 +227,24 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
   const int64_t i0 = (int64_t)ti * kTile;
   const int64_t j0 = (int64_t)tj * kTile;
   const int nk = (int)(a.Kc * esz / BK);
+  // LoRA epilogue: the tile's 256 rows of lora_b (i) and lora_xa (j), R bf16
+  // each, are copied to LDS past the operand ring now, long before the
+  // epilogue reads them as MFMA fragments.
+  uint8_t* const lora_lds = lds + STAGES * 2 * kTile * BK;
+  if constexpr (EPI == kEpiDequantLoraBf16) {
+    const int per_row = a.lora_r / 8;  // 16-byte pieces per row
+    for (int c = threadIdx.x; c < 2 * kTile * per_row; c += NT) {
+      const int op = c >= kTile * per_row;
+      const int cc = c - op * kTile * per_row;
+      const int row = cc / per_row, piece = cc % per_row;
+      int64_t g = (op ? j0 : i0) + row;
+      const int64_t lim = op ? a.J : a.I;
+      g = g < lim ? g : lim - 1;
+      const uint16_t* src = (op ? a.lora_xa : a.lora_b) + g * a.lora_r + 8 * piece;
+      *reinterpret_cast<uint4*>(lora_lds + (op * kTile + row) * a.lora_r * 2 + 16 * piece) =
+          *reinterpret_cast<const uint4*>(src);
+    }
+  }
 
   const uint8_t* P = static_cast<const uint8_t*>(a.P);
   const uint8_t* Q = static_cast<const uint8_t*>(a.Q);
@@ -433,6 +451,7 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
     constexpr int kRowBytes = TI * 2;
     constexpr int kChunkMask = TI / 8 - 1;
     static_assert(WI * WJ * TJ * kRowBytes <= STAGES * 2 * kStage, "staging fits the LDS ring");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes (LoRA rows) landed
     raw_barrier();  // all waves are done with the operand ring
     uint8_t* stg = lds + wave * TJ * kRowBytes;
     auto put8 = [&](int jl, int il, uint32_t lo, uint32_t hi) {
@@ -483,14 +502,30 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
         }
       }
     } else {
+      constexpr bool kDequant = EPI == kEpiDequantBf16 || EPI == kEpiDequantLoraBf16;
+      constexpr bool kLora = EPI == kEpiDequantLoraBf16;
+      // LoRA up projection: per 32 x 32 tile, lora_b rows (i) . lora_xa rows
+      // (j) over the rank with v_mfma_f32_32x32x16_bf16 (one or two k-steps),
+      // whose accumulator layout matches acc[x][y]; fragments come from the
+      // rows staged in LDS at the start of the tile.
+      auto lora_frag = [&](int op, int row, int kk) {
+        return *reinterpret_cast<const uint4*>(lora_lds + (op * kTile + row) * a.lora_r * 2 +
+                                               16 * h + 32 * kk);
+      };
 #pragma unroll
       for (int y = 0; y < NJ; ++y) {
         const int jl = y * 32 + (lane & 31);
         const int64_t j = j0 + wj * TJ + jl;
         float sjv = 1.f;
-        if constexpr (EPI == kEpiDequantBf16) sjv = j < a.J ? a.sj[j] : 0.f;
+        if constexpr (kDequant) sjv = j < a.J ? a.sj[j] : 0.f;
 #pragma unroll
         for (int x = 0; x < NI; ++x) {
+          v16f lo = {};
+          if constexpr (kLora) {
+            const int ri = wi * TI + x * 32 + (lane & 31), rj = wj * TJ + y * 32 + (lane & 31);
+            lo = mfma(lora_frag(0, ri, 0), lora_frag(1, rj, 0), lo);
+            if (a.lora_r > 16) lo = mfma(lora_frag(0, ri, 1), lora_frag(1, rj, 1), lo);
+          }
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int il = x * 32 + 8 * g + 4 * h;
@@ -498,7 +533,7 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
             float v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) v[u] = (float)acc[x][y][4 * g + u];
-            if constexpr (EPI == kEpiDequantBf16) {
+            if constexpr (kDequant) {
               if (i + 4 <= a.I) {
                 const float4 s4 = *reinterpret_cast<const float4*>(a.si + i);
                 v[0] = v[0] * sjv * s4.x;
@@ -519,6 +554,10 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
                   v[u] = v[u] + __uint_as_float((uint32_t)a.bias[iu] << 16);
                 }
               }
+            }
+            if constexpr (kLora) {
+#pragma unroll
+              for (int u = 0; u < 4; ++u) v[u] = v[u] + a.lora_scale * lo[4 * g + u];
             }
             put8(jl, il, pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
           }
@@ -552,7 +591,8 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
 
 template <int EPI, bool PT, bool BF16, int WI, int WJ, int BK, int STAGES>
 hipError_t launch(const GemmArgs& a, hipStream_t stream) {
-  constexpr int kLds = STAGES * 2 * kTile * BK;
+  // operand ring, plus the LoRA rows of one tile (2 x 256 rows x up to 32 bf16)
+  constexpr int kLds = STAGES * 2 * kTile * BK + (EPI == kEpiDequantLoraBf16 ? 2 * kTile * 64 : 0);
   auto kern = gemm_kernel<EPI, PT, BF16, WI, WJ, BK, STAGES>;
   static bool configured = false;
   if (!configured) {
@@ -582,6 +622,10 @@ hipError_t launch_gemm_i8(const GemmArgs& a, int epilogue, bool p_transposed, hi
   if (epilogue == kEpiI32) return launch<kEpiI32, false, false, kWI, kWJ, kBK, kStages>(a, stream);
   if (epilogue == kEpiDequantBf16)
     return launch<kEpiDequantBf16, false, false, kWI, kWJ, kBK, kStages>(a, stream);
+  if (epilogue == kEpiDequantLoraBf16) {
+    if (a.lora_r != 16 && a.lora_r != 32) return hipErrorInvalidValue;
+    return launch<kEpiDequantLoraBf16, false, false, kWI, kWJ, kBK, kStages>(a, stream);
+  }
   return hipErrorInvalidValue;
 }
 

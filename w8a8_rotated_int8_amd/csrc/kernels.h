@@ -27,6 +27,7 @@ enum GemmEpilogue {
   kEpiDequantBf16 = 1, // bf16( fl32(acc) * sj[j] * si[i] (+ bias[i]) )
   kEpiInvRotBf16 = 2,  // bf16( inverse-rotate along i of fl32(acc) * sj[j] )
   kEpiBf16 = 3,        // bf16(acc) of an fp32 accumulation
+  kEpiDequantLoraBf16 = 4,  // kEpiDequantBf16 + lora_scale * (lora_b[i] . lora_xa[j])
 };
 
 struct GemmArgs {
@@ -39,12 +40,21 @@ struct GemmArgs {
   const float* si;    // per-i scale (dequant epilogue)
   const float* sj;    // per-j scale
   const uint16_t* bias;  // per-i bf16 bias or nullptr
+  // LoRA epilogue only: lora_b [I, lora_r] and lora_xa [J, lora_r], bf16
+  const uint16_t* lora_b;
+  const uint16_t* lora_xa;
+  int lora_r;           // 16 or 32
+  float lora_scale;
 };
 
 // int8 operands (MFMA i32 32x32x32).  p_transposed: P is given as [Kc, I].
 hipError_t launch_gemm_i8(const GemmArgs& a, int epilogue, bool p_transposed, hipStream_t stream);
 // bf16 operands (MFMA f32 32x32x16), both row-major, kEpiBf16.
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t stream);
+
+// LoRA down projection xa [M, R] = bf16(x [M, K] . A [R, K]^T), R <= 32, K % 64 == 0.
+hipError_t launch_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint16_t* A, int R,
+                            uint16_t* xa, hipStream_t stream);
 
 // W_hat^T [K, N] bf16 from q_w [N, K], s_w [N].
 hipError_t launch_dequant_weight_t(const int8_t* qw, const float* sw, int64_t N, int64_t K,

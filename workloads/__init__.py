@@ -186,6 +186,15 @@ def qkv_weights(base: int = 0, N: int = 4096, K: int = 4096) -> list:
     return [packed_weight(1000 + j, base, N, K) for j in range(3)]
 
 
+def lora_weights(K: int, N: int, R: int, base: int = 0) -> dict:
+    """A trained-looking LoRA pair on its own seed streams: down A [R, K] and up
+    B [N, R], both ~N(0, 0.02) in bf16 (an untrained up projection would be 0)."""
+    g = np.random.Generator(np.random.PCG64([1000 * base + S_W, 2000 + R]))
+    a = f32_to_bf16_bits(g.standard_normal((R, K), dtype=np.float32) * np.float32(SIGMA_W))
+    b = f32_to_bf16_bits(g.standard_normal((N, R), dtype=np.float32) * np.float32(SIGMA_W))
+    return dict(a=a, b=b)
+
+
 EMBED_V, EMBED_D, EMBED_CHUNK, EMBED_T = 248320, 4096, 8192, 32768
 
 
