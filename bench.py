@@ -195,6 +195,7 @@ def main():
 
     if args.only == "all":
         extra.update(bench_qkv(cr, torch, dev, dev_normal, time_ms, wl))
+        extra.update(bench_small_m(cr, torch, dev, dev_normal, time_ms, wl))
         extra.update(bench_embedding(cr, torch, dev, dev_normal, time_ms, wl))
         extra.update(bench_mlp(cr, torch, dev, dev_normal, time_ms, wl))
         extra.update(bench_packed(cr, torch, dev, dev_normal, time_ms, wl))
@@ -258,6 +259,24 @@ def bench_qkv(cr, torch, dev, dev_normal, time_ms, wl):
     r = {"qkv_separate_us": round(t_sep * 1e3, 1), "qkv_separate_tops": round(ops / (t_sep * 1e-3) / 1e12, 1),
          "qkv_stacked_us": round(t_cat * 1e3, 1), "qkv_stacked_tops": round(ops / (t_cat * 1e-3) / 1e12, 1)}
     log(f"[bench] qkv {r}")
+    return r
+
+
+def bench_small_m(cr, torch, dev, dev_normal, time_ms, wl):
+    """Text-encoder shapes: one caption (M tokens) at a time, and skinny N = 32
+    outputs; these run the split-K forward."""
+    r = {}
+    log("[bench] small-M / skinny-N forwards")
+    for (M, K, N) in ((1, 4096, 4096), (77, 4096, 4096), (300, 4096, 4096), (77, 4096, 12288),
+                      (77, 4096, 32), (4096, 4096, 32)):
+        x = dev_normal((M, K), 1.0, 41)
+        qw, sw = cr.quantize_weight(dev_normal((N, K), wl.SIGMA_W, 42))
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(cr.workspace_bytes(cr.OP_LINEAR_FWD, M, N, K), dtype=torch.uint8, device=dev)
+        t = time_ms(lambda: cr.linear_fwd(x, qw, sw, out=y, workspace=ws), 10, 200)
+        r[f"fwd_{M}x{K}x{N}_us"] = round(t * 1e3, 2)
+        r[f"fwd_{M}x{K}x{N}_GBps_weights"] = round(N * K / (t * 1e-3) / 1e9, 1)
+    log(f"[bench] small-M {r}")
     return r
 
 

@@ -1,0 +1,72 @@
+"""Text-encoder shapes: one caption at a time (small, ragged M) and skinny
+outputs (N = 32), as in the training guide's text-encoder quantization
+(section 7.1, text encoder bullet).  With few 256 x 256 output tiles the
+forward splits the contraction (split-K) into int32 partials that one more
+launch sums and dequantizes.
+
+  * the split forward equals the one-pass stages (quantize_act + the int8 GEMM
+    with its dequantizing epilogue) bit for bit: integer partial sums are exact
+    and the epilogue's fp32 operations are the same;
+  * sampled rows match the oracle (1e-2 row tolerance; exact int32 sums).
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from gpu_util import assert_exact, assert_rows_close, bf16_to_dev, bits, host  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def cr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w8a8_rotated_int8_amd as cr
+    cr.lib()
+    return cr
+
+
+SHAPES = [(1, 4096, 4096), (7, 4096, 4096), (77, 4096, 4096), (300, 4096, 4096),
+          (77, 4096, 12288), (77, 12288, 4096), (77, 4096, 32), (4096, 4096, 32), (129, 512, 640)]
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_small_m_forward(cr, M, K, N):
+    import oracle
+    x = wl.activations(M, K, wl.n_outliers(K), base=0)
+    w = wl.packed_weight(4000 + N % 997, 0, N, K)
+    need = cr.workspace_bytes(cr.OP_LINEAR_FWD, M, N, K)
+    one_pass = ((M * K + 255) // 256) * 256 + ((4 * M + 255) // 256) * 256
+    print(f"M={M} K={K} N={N}: workspace {need} B ({'split' if need > one_pass else 'one pass'})",
+          flush=True)
+    qw, sw = cr.quantize_weight(bf16_to_dev(w))
+    xd = bf16_to_dev(x)
+    y = cr.linear_fwd(xd, qw, sw)
+    qx, sx = cr.quantize_act(xd)
+    y1 = cr.gemm_i8_bf16(qx, sx, qw, sw)
+    assert torch.equal(y, y1), "split forward differs from the one-pass stages"
+    g = np.random.default_rng(71 + M)
+    rows = np.unique(np.concatenate([[0, M - 1], g.choice(M, min(M, 6), replace=False)]))
+    oqx, osx, _ = oracle.rotate_quantize(x[rows])
+    oqw, osw, _ = oracle.rotate_quantize(w)
+    assert_exact(host(qx)[rows], oqx, "q_x (sampled rows)")
+    oacc = oracle.gemm_i8_i32(oqx, oqw)
+    assert_exact(host(cr.gemm_i8_i32(qx, qw, 0))[rows], oacc, "acc (sampled rows)")
+    e = assert_rows_close(bits(y)[rows], oracle.dequant_epilogue(oacc, osx, osw), "y (sampled rows)")
+    print(f"  max row relerr {e:.2e}", flush=True)
+
+
+def test_small_m_with_bias(cr):
+    M, K, N = 77, 4096, 4096
+    x = wl.activations(M, K, wl.n_outliers(K), base=1)
+    w = wl.packed_weight(4100, 1, N, K)
+    bias = bf16_to_dev(wl.normal_bf16((N,), 1.0, 1, 18))
+    qw, sw = cr.quantize_weight(bf16_to_dev(w))
+    xd = bf16_to_dev(x)
+    y = cr.linear_fwd(xd, qw, sw, bias=bias)
+    qx, sx = cr.quantize_act(xd)
+    assert torch.equal(y, cr.gemm_i8_bf16(qx, sx, qw, sw, bias=bias))

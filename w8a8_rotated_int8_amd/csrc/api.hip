@@ -55,6 +55,12 @@ int quantize_rows_checked(const uint16_t* x, int64_t rows, int64_t K, int8_t* q,
 }
 
 size_t fwd_workspace(int64_t M, int64_t K) { return align256((size_t)M * K) + align256(4 * (size_t)M); }
+// The forward also holds the int32 partials of a split-K GEMM when the shape
+// has too few output tiles to fill the chip (small M, or skinny N).
+size_t fwd_splitk_workspace(int64_t M, int64_t N, int64_t K) {
+  const int S = splitk_factor(M, N, K);
+  return S > 1 ? align256((size_t)S * M * N * 4) : 0;
+}
 size_t bwd_int8_workspace(int64_t M, int64_t N) {
   return align256((size_t)M * N) + align256(4 * (size_t)M);
 }
@@ -81,7 +87,7 @@ const char* convrot_status_string(int status) {
 
 size_t convrot_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t mode) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  if (op == CONVROT_OP_LINEAR_FWD) return fwd_workspace(M, K);
+  if (op == CONVROT_OP_LINEAR_FWD) return fwd_workspace(M, K) + fwd_splitk_workspace(M, N, K);
   if (op == CONVROT_OP_LINEAR_FWD_LORA)
     return (mode == 16 || mode == 32) ? fwd_workspace(M, K) + align256(2 * (size_t)M * mode) : 0;
   if (op == CONVROT_OP_LINEAR_BWD_DX) {
@@ -129,7 +135,8 @@ int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw
       (reinterpret_cast<uintptr_t>(workspace) & 255))
     return CONVROT_EINVAL;
   if (!row_len_ok(K)) return CONVROT_ESHAPE;
-  if (workspace_bytes < fwd_workspace(M, K)) return CONVROT_EWORKSPACE;
+  if (workspace_bytes < fwd_workspace(M, K) + fwd_splitk_workspace(M, N, K))
+    return CONVROT_EWORKSPACE;
   int st = check_device();
   if (st) return st;
   int8_t* qx = static_cast<int8_t*>(workspace);
@@ -139,6 +146,11 @@ int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw
   GemmArgs a{};
   a.P = qw; a.Q = qx; a.I = N; a.J = M; a.Kc = K; a.ldp = K; a.ldq = K;
   a.out = y; a.ldo = N; a.si = sw; a.sj = sx; a.bias = bias;
+  const int S = splitk_factor(M, N, K);
+  if (S > 1) {
+    int32_t* partial = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + fwd_workspace(M, K));
+    return hip_status(launch_gemm_i8_splitk_dequant(a, S, partial, stream));
+  }
   return hip_status(launch_gemm_i8(a, kEpiDequantBf16, false, stream));
 }
 

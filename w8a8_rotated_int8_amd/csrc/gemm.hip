@@ -190,9 +190,11 @@ __device__ __forceinline__ void store_transposed(const TransposedRegs& t, uint8_
 }
 
 // Dispatch id -> (i tile, j tile), XCD-aware (see the file comment).
-__device__ __forceinline__ void tile_of(int64_t gi, int64_t gj, int& ti, int& tj) {
+// `tile` is the launch-order index of the tile (the dispatch id of a
+// one-tile-per-workgroup launch).
+__device__ __forceinline__ void tile_of(int64_t gi, int64_t gj, int64_t tile, int& ti, int& tj) {
   const int64_t nb = gi * gj;
-  int64_t b = blockIdx.x;
+  int64_t b = tile;
   if (nb % kNumXcd == 0) b = (b % kNumXcd) * (nb / kNumXcd) + b / kNumXcd;
   const int64_t G = CONVROT_GEMM_GROUP_J;
   const int64_t per_group = G * gi;
@@ -204,9 +206,39 @@ __device__ __forceinline__ void tile_of(int64_t gi, int64_t gj, int& ti, int& tj
   ti = (int)(r / gsize);
 }
 
+// Dequantizing epilogue of four consecutive outputs i .. i+3 of row j:
+// v = fl32(acc) * s_j * s_i (+ bias_i), each operation rounded to fp32 in this
+// order (no contraction), so every path that uses it rounds identically.
+__device__ __forceinline__ void dequant4(float v[4], float sjv, const float* si,
+                                         const uint16_t* bias, int64_t i, int64_t I) {
+#pragma clang fp contract(off)
+  if (i + 4 <= I) {
+    const float4 s4 = *reinterpret_cast<const float4*>(si + i);
+    v[0] = v[0] * sjv * s4.x;
+    v[1] = v[1] * sjv * s4.y;
+    v[2] = v[2] * sjv * s4.z;
+    v[3] = v[3] * sjv * s4.w;
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t iu = i + u < I ? i + u : I - 1;
+      v[u] = v[u] * sjv * si[iu];
+    }
+  }
+  if (bias) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t iu = i + u < I ? i + u : I - 1;
+      v[u] = v[u] + __uint_as_float((uint32_t)bias[iu] << 16);
+    }
+  }
+}
+
+// One 256 x 256 output tile; every thread of the workgroup takes part.  LDS at
+// `lds`: the operand ring (STAGES * 2 * 256 * BK bytes), plus 32 KB for the
+// LoRA epilogue.
 template <int EPI, bool PT, bool BF16, int WI, int WJ, int BK, int STAGES>
-__global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
-  extern __shared__ __align__(16) uint8_t lds[];
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8_t* lds) {
   typedef typename AccT<BF16>::type acc_t;
   constexpr int esz = BF16 ? 2 : 1;
   constexpr int NT = 64 * WI * WJ;
@@ -223,7 +255,7 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
   const int wi = wave % WI, wj = wave / WI;
   const int64_t gi = (a.I + kTile - 1) / kTile, gj = (a.J + kTile - 1) / kTile;
   int ti, tj;
-  tile_of(gi, gj, ti, tj);
+  tile_of(gi, gj, tile, ti, tj);
   const int64_t i0 = (int64_t)ti * kTile;
   const int64_t j0 = (int64_t)tj * kTile;
   const int nk = (int)(a.Kc * esz / BK);
@@ -533,28 +565,7 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
             float v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) v[u] = (float)acc[x][y][4 * g + u];
-            if constexpr (kDequant) {
-              if (i + 4 <= a.I) {
-                const float4 s4 = *reinterpret_cast<const float4*>(a.si + i);
-                v[0] = v[0] * sjv * s4.x;
-                v[1] = v[1] * sjv * s4.y;
-                v[2] = v[2] * sjv * s4.z;
-                v[3] = v[3] * sjv * s4.w;
-              } else {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                  const int64_t iu = i + u < a.I ? i + u : a.I - 1;
-                  v[u] = v[u] * sjv * a.si[iu];
-                }
-              }
-              if (a.bias) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                  const int64_t iu = i + u < a.I ? i + u : a.I - 1;
-                  v[u] = v[u] + __uint_as_float((uint32_t)a.bias[iu] << 16);
-                }
-              }
-            }
+            if constexpr (kDequant) dequant4(v, sjv, a.si, a.bias, i, a.I);
             if constexpr (kLora) {
 #pragma unroll
               for (int u = 0; u < 4; ++u) v[u] = v[u] + a.lora_scale * lo[4 * g + u];
@@ -587,6 +598,55 @@ __global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
       }
     }
   }
+}
+
+template <int EPI, bool PT, bool BF16, int WI, int WJ, int BK, int STAGES>
+__global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  gemm_tile<EPI, PT, BF16, WI, WJ, BK, STAGES>(a, blockIdx.x, lds);
+}
+
+// Split-K: workgroup (slice s, tile t) with blockIdx = s * tiles + t contracts
+// K-slice s of both row-major int8 operands into the int32 partial tile
+// partial[s] ([J, I], row stride I).
+template <int WI, int WJ, int BK, int STAGES>
+__global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_splitk_kernel(GemmArgs a, int64_t tiles,
+                                                                      int64_t k_slice,
+                                                                      int32_t* partial) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int64_t s = blockIdx.x / tiles;
+  GemmArgs b = a;
+  b.P = static_cast<const int8_t*>(a.P) + s * k_slice;
+  b.Q = static_cast<const int8_t*>(a.Q) + s * k_slice;
+  b.Kc = k_slice;
+  b.out = partial + s * a.J * a.I;
+  b.ldo = a.I;
+  gemm_tile<kEpiI32, false, false, WI, WJ, BK, STAGES>(b, blockIdx.x % tiles, lds);
+}
+
+// y[j][i..i+3] = dequant4( sum_s partial[s][j][i..i+3] ) as bf16; one thread
+// per 4 outputs (I % 4 == 0).
+__global__ __launch_bounds__(256) void splitk_dequant_kernel(const int32_t* __restrict__ partial,
+                                                             int S, int64_t J, int64_t I,
+                                                             const float* __restrict__ si,
+                                                             const float* __restrict__ sj,
+                                                             const uint16_t* __restrict__ bias,
+                                                             uint16_t* __restrict__ out) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // quad index
+  const int64_t per_row = I / 4;
+  if (q >= J * per_row) return;
+  const int64_t j = q / per_row, i = 4 * (q % per_row);
+  int4 acc = *reinterpret_cast<const int4*>(partial + j * I + i);
+  for (int s = 1; s < S; ++s) {
+    const int4 p = *reinterpret_cast<const int4*>(partial + (s * J + j) * I + i);
+    acc.x += p.x;
+    acc.y += p.y;
+    acc.z += p.z;
+    acc.w += p.w;
+  }
+  float v[4] = {(float)acc.x, (float)acc.y, (float)acc.z, (float)acc.w};
+  dequant4(v, sj[j], si, bias, i, I);
+  *reinterpret_cast<uint2*>(out + j * I + i) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
 template <int EPI, bool PT, bool BF16, int WI, int WJ, int BK, int STAGES>
@@ -627,6 +687,55 @@ hipError_t launch_gemm_i8(const GemmArgs& a, int epilogue, bool p_transposed, hi
     return launch<kEpiDequantLoraBf16, false, false, kWI, kWJ, kBK, kStages>(a, stream);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_i8_splitk_dequant(const GemmArgs& a, int S, int32_t* partial,
+                                         hipStream_t stream) {
+  if (S < 1 || a.Kc % (S * kBK) || a.I % 4) return hipErrorInvalidValue;
+  constexpr int kLds = kStages * 2 * kTile * kBK;
+  auto kern = gemm_splitk_kernel<kWI, kWJ, kBK, kStages>;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const int64_t gi = (a.I + kTile - 1) / kTile, gj = (a.J + kTile - 1) / kTile;
+  const int64_t tiles = gi * gj;
+  if (tiles <= 0) return hipSuccess;
+  if (tiles * S > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * S)), dim3(64 * kWI * kWJ), kLds, stream, a, tiles,
+                     a.Kc / S, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t quads = a.J * (a.I / 4);
+  const int64_t blocks = (quads + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(splitk_dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, partial, S,
+                     a.J, a.I, a.si, a.sj, a.bias, static_cast<uint16_t*>(a.out));
+  return hipGetLastError();
+}
+
+int splitk_factor(int64_t M, int64_t N, int64_t K) {
+  // Pick S (a divisor of K/128, at most 32) minimising a simple cost model of
+  // the split launch: waves of 256 workgroups over a K-slice each (~10.7 ns per
+  // contraction byte of one tile, measured), plus writing and reading the
+  // int32 partials at ~5 TB/s.  S = 1 keeps the one-pass GEMM.
+  const int64_t tiles = ((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile);
+  if (tiles >= 128 || N % 4) return 1;
+  const int64_t kb = K / kBlock;
+  int best = 1;
+  double best_t = 0.0;
+  for (int S = 1; S <= 32 && S <= kb; ++S) {
+    if (kb % S) continue;
+    const double waves = (double)((tiles * S + 255) / 256);
+    const double t = waves * (double)(K / S) * 0.0107 + (S > 1 ? (double)S * M * N * 8.0 / 5.0e6 : 0.0);
+    if (S == 1 || t < best_t) {
+      best = S;
+      best_t = t;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t stream) {

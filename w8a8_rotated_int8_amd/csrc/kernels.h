@@ -49,6 +49,15 @@ struct GemmArgs {
 
 // int8 operands (MFMA i32 32x32x32).  p_transposed: P is given as [Kc, I].
 hipError_t launch_gemm_i8(const GemmArgs& a, int epilogue, bool p_transposed, hipStream_t stream);
+// Split-K int8 GEMM with the dequantizing epilogue (kEpiDequantBf16
+// semantics, bit-identical results): S K-slices into int32 partials
+// [S, J, I] (caller-provided), then one reduce + dequantize launch.  Needs
+// Kc % (S * 128) == 0 and I % 4 == 0.
+hipError_t launch_gemm_i8_splitk_dequant(const GemmArgs& a, int S, int32_t* partial,
+                                         hipStream_t stream);
+// Split count for a forward of M tokens, N outputs, K inputs (1 = no split).
+int splitk_factor(int64_t M, int64_t N, int64_t K);
+
 // bf16 operands (MFMA f32 32x32x16), both row-major, kEpiBf16.
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t stream);
 
