@@ -67,8 +67,9 @@ def crafted_rows(K: int) -> np.ndarray:
 # Quantizer (weights, activations, embedding chunks)
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,K", [(1, 128), (3, 256), (64, 256), (301, 384), (97, 4096),
-                                 (33, 4224), (16, 12288), (24, 16384), (5, 32768)])
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 256), (64, 256), (301, 384), (40, 512),
+                                 (37, 1024), (19, 1152), (23, 1920), (31, 2048), (9, 2176),
+                                 (97, 4096), (33, 4224), (16, 12288), (24, 16384), (5, 32768)])
 def test_quantize_act_exact(cr, orc, M, K):
     say(f"quantize_act M={M} K={K}")
     x = wl.activations(M, K, max(1, wl.n_outliers(K)), base=M + K)

@@ -84,10 +84,50 @@ __device__ __forceinline__ void swap_halves(float& vdst, float& src0) {
   src0 = __uint_as_float(b);
 }
 
-// Wave-wide butterfly max over lanes xor `mask` for masks 1..limit/2.
-__device__ __forceinline__ float wave_max_xor(float v, int limit) {
-  for (int o = 1; o < limit; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// Cross-lane maxima of non-negative, non-NaN floats (row maxima of |r| that
+// start from +0 under fmaxf, which drops NaN): on such values the order of the
+// bit patterns as unsigned integers is the order of the floats, so the lanes
+// combine with integer max and no NaN canonicalisation is needed.
+//
+// DPP lane patterns within each 16-lane row (gfx9 dpp_ctrl encodings).
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]: lane i <- i ^ 1
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]: lane i <- i ^ 2
+constexpr int kDppRowMirror = 0x140;   // lane i <- 15 - i within the row
+constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within each 8 lanes
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t max_dpp(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+  return v > o ? v : o;
+}
+
+// Max over aligned groups of n consecutive lanes (n = 1, 2, 4, 8 or 16) of each
+// 16-lane row; every lane of a group receives its group's max.  After the two
+// quad steps a lane holds its quad's max; the half-row mirror pairs each quad
+// with the other quad of its 8 lanes, the row mirror each 8 with the other 8.
+__device__ __forceinline__ float group_max(float v, int n) {
+  uint32_t u = __float_as_uint(v);
+  if (n > 1) u = max_dpp<kDppQuadXor1>(u);
+  if (n > 2) u = max_dpp<kDppQuadXor2>(u);
+  if (n > 4) u = max_dpp<kDppHalfMirror>(u);
+  if (n > 8) u = max_dpp<kDppRowMirror>(u);
+  return __uint_as_float(u);
+}
+
+// Max with the lane 16 apart (rows 0 and 1, rows 2 and 3).  permlane16_swap of
+// a value with itself leaves rows (0,0,2,2) in one result and (1,1,3,3) in the
+// other.
+__device__ __forceinline__ float max_xor16(float v) {
+  const uint32_t u = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0] > r[1] ? r[0] : r[1]);
+}
+
+// Max with the lane 32 apart (the two wave halves).
+__device__ __forceinline__ float max_xor32(float v) {
+  const uint32_t u = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0] > r[1] ? r[0] : r[1]);
 }
 
 // Wait for all outstanding vector-memory operations of this wave (including

@@ -17,70 +17,73 @@
 namespace convrot {
 namespace {
 
-#ifndef CONVROT_RQ_WAVES
-#define CONVROT_RQ_WAVES 2
+#ifndef CONVROT_SPAN
+#define CONVROT_SPAN 16
 #endif
+// Blocks per wave span.  With 16 a wave holds 32 values per lane and fits in
+// 128 VGPRs, so four waves share a SIMD (32: two passes, ~150 VGPRs, three).
+constexpr int kSpan = CONVROT_SPAN;
 
-constexpr int kMaxWavesPerRow = CONVROT_MAX_ROW_LEN_BLOCKS / kSpanBlocks;
-
-// Short rows (K <= 4096): one task of rows_per_wave packed rows per wave, in
-// its own 8 KB LDS buffer; several resident waves per SIMD cover each other's
-// load latency.
-template <int MODE>
-__global__ __launch_bounds__(256, CONVROT_RQ_WAVES) void rotate_quant_rows_kernel(
+// Short rows (K < 128 * kSpan): one task of rows_per_wave packed rows per wave,
+// in its own LDS buffer; the resident waves of a SIMD cover each other's load
+// latency.
+template <int MODE, int SB>
+__global__ __launch_bounds__(256) void rotate_quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int K, int8_t* __restrict__ q,
     float* __restrict__ scale, const float* __restrict__ colscale, int rows_per_wave) {
   extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ float seg_max[4][kSpanBlocks];
+  __shared__ float seg_max[4][SB];
   const int wave = threadIdx.x >> 6;
   const int nb = K / kBlock;
   const int64_t ntasks = (rows + rows_per_wave - 1) / rows_per_wave;
   const int64_t task = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
   if (task >= ntasks) return;
-  uint8_t* buf = lds + wave * kSpanBytes;
+  uint8_t* buf = lds + wave * span_bytes<SB>();
   const int64_t r0 = task * rows_per_wave;
   const int64_t rh = rows - r0;
   const int nbk = (rh < rows_per_wave ? (int)rh : rows_per_wave) * nb;
-  stage_span(x, r0 * (int64_t)K, nbk, buf);
+  stage_span<SB>(x, r0 * (int64_t)K, nbk, buf);
   wait_vm_n<0>();
-  quantize_span<MODE>(buf, nbk, nb, r0 * (int64_t)K, 0, r0, 1, q, scale, colscale,
-                      seg_max[wave], nullptr);
+  quantize_span<MODE, SB>(buf, nbk, nb, r0 * (int64_t)K, 0, r0, 1, q, scale, colscale,
+                          seg_max[wave], nullptr);
 }
 
-// Long rows (K > 4096): one row per workgroup, one 4096-wide slice per wave;
-// the waves combine their maxima through LDS.
-template <int MODE>
-__global__ __launch_bounds__(512) void rotate_quant_long_kernel(
+// Long rows (K >= 128 * kSpan): one row per workgroup, one SB-block slice per
+// wave; the waves combine their maxima through LDS.
+template <int MODE, int SB>
+__global__ __launch_bounds__(SB == 16 ? 1024 : 512) void rotate_quant_long_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int K, int8_t* __restrict__ q,
     float* __restrict__ scale, const float* __restrict__ colscale, int waves_per_row) {
   extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ float row_part_max[kMaxWavesPerRow];
+  __shared__ float row_part_max[CONVROT_MAX_ROW_LEN_BLOCKS / SB];
   const int wave = threadIdx.x >> 6;
   const int nb = K / kBlock;
   const int64_t row0 = blockIdx.x;
-  const int blk_in_row0 = wave * kSpanBlocks;
+  const int blk_in_row0 = wave * SB;
   const int rem = nb - blk_in_row0;
-  const int span_blocks = rem < kSpanBlocks ? rem : kSpanBlocks;
+  const int span_blocks = rem < SB ? rem : SB;
   const int64_t span_elem0 = row0 * (int64_t)K + (int64_t)blk_in_row0 * kBlock;
-  uint8_t* my_lds = lds + wave * kSpanBytes;
-  stage_span(x, span_elem0, span_blocks, my_lds);
+  uint8_t* my_lds = lds + wave * span_bytes<SB>();
+  stage_span<SB>(x, span_elem0, span_blocks, my_lds);
   wait_vm_n<0>();
-  quantize_span<MODE>(my_lds, span_blocks, nb, span_elem0, blk_in_row0, row0, waves_per_row, q,
-                      scale, colscale, nullptr, row_part_max);
+  quantize_span<MODE, SB>(my_lds, span_blocks, nb, span_elem0, blk_in_row0, row0, waves_per_row,
+                          q, scale, colscale, nullptr, row_part_max);
 }
 
 }  // namespace
 
+// Rows shorter than a span are packed into one; longer rows are split into
+// span-wide slices, one per wave.
 RowPlan plan_rows(int K) {
   RowPlan pl;
   int nb = K / kBlock;
-  if (nb <= kSpanBlocks) {
-    pl.rows_per_wave = kSpanBlocks / nb;
+  if (nb < kSpan) {
+    pl.rows_per_wave = kSpan / nb;
     pl.waves_per_row = 1;
     pl.threads = 256;
   } else {
     pl.rows_per_wave = 1;
-    pl.waves_per_row = (nb + kSpanBlocks - 1) / kSpanBlocks;
+    pl.waves_per_row = (nb + kSpan - 1) / kSpan;
     pl.threads = 64 * pl.waves_per_row;
   }
   return pl;
@@ -90,42 +93,40 @@ hipError_t launch_rotate_quant(const uint16_t* x, int64_t rows, int K, int8_t* q
                                const float* colscale, bool fold, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   RowPlan pl = plan_rows(K);
-  static int n_cu = 0;
   static bool configured = false;
   if (!configured) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    const int max_lds = kMaxWavesPerRow * kSpanBytes;
-    const void* ks[2] = {(const void*)rotate_quant_long_kernel<kRotate>,
-                         (const void*)rotate_quant_long_kernel<kFold>};
+    hipError_t e = hipSuccess;
+    const int max_lds = CONVROT_MAX_ROW_LEN_BLOCKS * 256;
+    const void* ks[2] = {(const void*)rotate_quant_long_kernel<kRotate, kSpan>,
+                         (const void*)rotate_quant_long_kernel<kFold, kSpan>};
     for (const void* k : ks) {
       e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
       if (e != hipSuccess) return e;
     }
     configured = true;
   }
-  if (pl.waves_per_row == 1) {
+  if (K / kBlock < kSpan) {
     const int64_t tasks = (rows + pl.rows_per_wave - 1) / pl.rows_per_wave;
     const int64_t grid = (tasks + 3) / 4;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    const size_t lds = 4 * kSpanBytes;
+    const size_t lds = 4 * span_bytes<kSpan>();
     if (fold)
-      hipLaunchKernelGGL(rotate_quant_rows_kernel<kFold>, dim3((unsigned)grid), dim3(256), lds,
-                         stream, x, rows, K, q, scale, colscale, pl.rows_per_wave);
+      hipLaunchKernelGGL((rotate_quant_rows_kernel<kFold, kSpan>), dim3((unsigned)grid), dim3(256),
+                         lds, stream, x, rows, K, q, scale, colscale, pl.rows_per_wave);
     else
-      hipLaunchKernelGGL(rotate_quant_rows_kernel<kRotate>, dim3((unsigned)grid), dim3(256), lds,
-                         stream, x, rows, K, q, scale, colscale, pl.rows_per_wave);
+      hipLaunchKernelGGL((rotate_quant_rows_kernel<kRotate, kSpan>), dim3((unsigned)grid), dim3(256),
+                         lds, stream, x, rows, K, q, scale, colscale, pl.rows_per_wave);
   } else {
     if (rows > 0x7fffffff) return hipErrorInvalidValue;
-    const size_t lds = (size_t)pl.waves_per_row * kSpanBytes;
+    const size_t lds = (size_t)pl.waves_per_row * span_bytes<kSpan>();
     if (fold)
-      hipLaunchKernelGGL(rotate_quant_long_kernel<kFold>, dim3((unsigned)rows), dim3(pl.threads),
-                         lds, stream, x, rows, K, q, scale, colscale, pl.waves_per_row);
+      hipLaunchKernelGGL((rotate_quant_long_kernel<kFold, kSpan>), dim3((unsigned)rows),
+                         dim3(pl.threads), lds, stream, x, rows, K, q, scale, colscale,
+                         pl.waves_per_row);
     else
-      hipLaunchKernelGGL(rotate_quant_long_kernel<kRotate>, dim3((unsigned)rows), dim3(pl.threads),
-                         lds, stream, x, rows, K, q, scale, colscale, pl.waves_per_row);
+      hipLaunchKernelGGL((rotate_quant_long_kernel<kRotate, kSpan>), dim3((unsigned)rows),
+                         dim3(pl.threads), lds, stream, x, rows, K, q, scale, colscale,
+                         pl.waves_per_row);
   }
   return hipGetLastError();
 }

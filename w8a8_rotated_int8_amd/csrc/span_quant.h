@@ -1,6 +1,6 @@
 // Span quantizer: the device-side rotate (or scale-fold) + per-row int8
-// quantization of up to 32 consecutive 128-blocks held in LDS.  Shared by the
-// standalone quantizer kernels and the single-launch forward.
+// quantization of a span of up to SB (16 or 32) consecutive 128-blocks held in
+// LDS, used by the row quantizer kernels.
 //
 // Arithmetic (bit-exact by construction):
 //   rotate:   per 128-block, S_j = sum_i H[i][j] x_i computed by a fast
@@ -12,17 +12,16 @@
 //   quantize: a = max|r|, s = fl32(a/127), code = RNE(fl32(r/s)); all-zero row
 //             -> s = 0, codes 0.
 //
-// Work layout.  A wave owns a span of up to 32 consecutive 128-blocks (4096
-// elements): one row of K = 4096, several short rows packed together, or a
-// 4096-wide slice of a long row (then the workgroup's waves share the row and
-// combine their maxima through LDS).  The span is copied to LDS with direct
-// 16-byte global->LDS loads (coalesced, XOR-swizzled so the transposed reads
-// are bank-conflict free) and processed in two passes of 16 blocks: in pass k
-// lane 16 g + p holds elements 32 g .. 32 g + 31 of block 16 k + p.  Five
-// butterfly stages run inside the lane, the sixth pairs lane L with L + 16
-// (v_permlane16_swap) and the seventh with L + 32 (v_permlane32_swap).  With
-// 32 values per lane a wave needs ~150 VGPRs, so three waves share a SIMD and
-// cover each other's load latency.
+// Work layout.  A wave owns a span of SB blocks: several short rows packed
+// together, or an SB-block slice of a longer row (then the workgroup's waves
+// share the row and combine their maxima through LDS).  The span is copied to
+// LDS with direct 16-byte global->LDS loads (coalesced, XOR-swizzled so the
+// transposed reads are bank-conflict free) and processed in passes of 16
+// blocks: in pass k lane 16 g + p holds elements 32 g .. 32 g + 31 of block
+// 16 k + p.  Five butterfly stages run inside the lane, the sixth pairs lane L
+// with L + 16 (v_permlane16_swap) and the seventh with L + 32
+// (v_permlane32_swap).  A 16-block span keeps 32 values per lane and fits in
+// ~100 VGPRs (four waves per SIMD); a 32-block span keeps 64 (~150 VGPRs).
 #pragma once
 
 #include "common.h"
@@ -31,10 +30,16 @@
 namespace convrot {
 namespace {
 
-constexpr int kSpanBlocks = 32;                  // blocks per wave span
-constexpr int kSpanBytes = kSpanBlocks * 256;    // bf16 bytes per wave span
+constexpr int kSpanBlocks = 32;                  // largest span (blocks per wave)
+constexpr int kSpanBytes = kSpanBlocks * 256;    // bf16 bytes of the largest span
+
+// bf16 bytes of a span of SB blocks.
+template <int SB>
+constexpr int span_bytes() { return SB * 256; }
 
 enum Mode { kRotate = 0, kFold = 1 };
+
+constexpr float kInv127 = 0x1.020408p-7f;  // RN(1/127)
 
 // LDS position (in 16-byte units) of chunk c (0..15) of block b.
 __device__ __forceinline__ int lds_chunk(int b, int c) { return (b << 4) | (c ^ (b & 7)); }
@@ -58,7 +63,7 @@ __device__ __forceinline__ void swap_rows16(double& vdst, double& src0) {
 // register bit 4 with a lane bit, so that the butterfly partners meet in one
 // lane.  After both, lane quarter q = L >> 4 holds outputs 16 q + e in v[e]
 // and 64 + 16 q + e in v[e + 16] (e < 16).
-template <int MODE>
+template <int MODE, int SB = kSpanBlocks>
 __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_blocks, int nb,
                                               int64_t span_elem0, int blk_in_row0, int64_t row0,
                                               int waves_per_row, int8_t* __restrict__ q,
@@ -66,14 +71,16 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
                                               const float* __restrict__ colscale,
                                               float* seg_max_wave, float* row_part_max) {
 #pragma clang fp contract(off)
+  static_assert(SB == 16 || SB == 32, "a span is one or two passes of 16 blocks");
+  constexpr int NP = SB / 16;  // passes
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int p = lane & 15;   // block within the pass
   const int g = lane >> 4;   // which quarter of the block
 
-  float r[2][32];
+  float r[NP][32];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < NP; ++k) {
     // keep the two passes apart: interleaving them would hold both passes'
     // binary64 working sets at once
     __builtin_amdgcn_sched_barrier(0);
@@ -158,46 +165,51 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
   }
 
   // ---- row absmax ------------------------------------------------------------
-  float m[2] = {0.f, 0.f};
+  float m[NP];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < NP; ++k) {
+    m[k] = 0.f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) m[k] = fmaxf(m[k], fabsf(r[k][e]));
-    m[k] = fmaxf(m[k], __shfl_xor(m[k], 16, kWave));  // the four quarters of the block
-    m[k] = fmaxf(m[k], __shfl_xor(m[k], 32, kWave));
+    m[k] = max_xor32(max_xor16(m[k]));  // the four quarters of the block
   }
+  float mall = m[0];
+#pragma unroll
+  for (int k = 1; k < NP; ++k) mall = fmaxf(mall, m[k]);
   if (waves_per_row == 1) {
-    if (nb == 32) {
-      const float mm = wave_max_xor(fmaxf(m[0], m[1]), 16);
-      m[0] = m[1] = mm;
+    if (nb == SB) {
+      const float mm = group_max(mall, 16);
+#pragma unroll
+      for (int k = 0; k < NP; ++k) m[k] = mm;
     } else if ((nb & (nb - 1)) == 0) {
-      m[0] = wave_max_xor(m[0], nb);       // aligned segments of nb blocks
-      m[1] = wave_max_xor(m[1], nb);
+#pragma unroll
+      for (int k = 0; k < NP; ++k) m[k] = group_max(m[k], nb);  // aligned segments of nb blocks
     } else {
       if (g == 0) {
-        seg_max_wave[p] = m[0];
-        seg_max_wave[16 + p] = m[1];
+#pragma unroll
+        for (int k = 0; k < NP; ++k) seg_max_wave[16 * k + p] = m[k];
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < NP; ++k) {
         const int first = ((16 * k + p) / nb) * nb;
         float mm = 0.f;
         for (int j = 0; j < nb; ++j) {
           const int idx = first + j;
-          if (idx < kSpanBlocks) mm = fmaxf(mm, seg_max_wave[idx]);
+          if (idx < SB) mm = fmaxf(mm, seg_max_wave[idx]);
         }
         m[k] = mm;
       }
     }
   } else {
-    const float mw = wave_max_xor(fmaxf(m[0], m[1]), 16);
+    const float mw = group_max(mall, 16);
     if (lane == 0) row_part_max[wave] = mw;
     __syncthreads();
     float mm = 0.f;
     for (int w = 0; w < waves_per_row; ++w) mm = fmaxf(mm, row_part_max[w]);
-    m[0] = m[1] = mm;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) m[k] = mm;
   }
 
   // ---- quantize + stage + store -------------------------------------------------
@@ -207,18 +219,23 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
   uint8_t* stg = const_cast<uint8_t*>(my_lds);
   auto phys = [](int c) { return c ^ ((c >> 3) & 7); };
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < NP; ++k) {
     const int b = 16 * k + p;
-    const float s = m[k] / 127.0f;                     // IEEE binary32 division
-    const bool fast = s > 0x1p-100f && s < 0x1p100f;
-    const float inv = s > 0.f ? 1.0f / s : 0.f;        // RN(1/s)
-    // Quotients: the 3-operation correctly rounded form when every lane's row
-    // scale is in range (wave-uniform branch), else the IEEE division per lane.
-    float t[32];
+    // s = fl32(m / 127) and the quotients fl32(r / s), both correctly rounded.
+    // When every lane's row max is in [2^-64, 2^100] (wave-uniform branch) both
+    // use the 3-operation form with the correctly rounded reciprocal (for the
+    // divisor 127 checked exhaustively over all significands); otherwise the
+    // IEEE division per lane.
+    const bool fast = m[k] >= 0x1p-64f && m[k] <= 0x1p100f;
+    float s, t[32];
     if (__builtin_amdgcn_ballot_w64(!fast) == 0) {
+      s = quot_rn(m[k], 127.0f, kInv127);
+      const float inv = 1.0f / s;                      // RN(1/s)
 #pragma unroll
       for (int e = 0; e < 32; ++e) t[e] = quot_rn(r[k][e], s, inv);
     } else {
+      s = m[k] / 127.0f;                               // IEEE binary32 division
+      const float inv = s > 0.f ? 1.0f / s : 0.f;
 #pragma unroll
       for (int e = 0; e < 32; ++e) t[e] = fast ? quot_rn(r[k][e], s, inv) : (s > 0.f ? r[k][e] / s : 0.f);
     }
@@ -243,22 +260,23 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
   const int nchunks = span_blocks * 8;
   int8_t* dst = q + span_elem0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < SB / 8; ++j) {
     const int c = 64 * j + lane;
     if (c < nchunks)
       *reinterpret_cast<uint4*>(dst + 16 * c) = *reinterpret_cast<const uint4*>(stg + 16 * phys(c));
   }
 }
 
-// Issue the 8 direct-to-LDS loads of a span of span_blocks (>= 1) blocks.
+// Issue the SB/4 direct-to-LDS loads of a span of span_blocks (1..SB) blocks.
 // Slots past the span reload its last chunk so every lane always issues the
 // same number of loads (the vmcnt bookkeeping relies on it).
+template <int SB = kSpanBlocks>
 __device__ __forceinline__ void stage_span(const uint16_t* __restrict__ x, int64_t span_elem0,
                                            int span_blocks, uint8_t* my_lds) {
   const int lane = threadIdx.x & 63;
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_u32(my_lds));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < SB / 4; ++i) {
     const int slot = i * 64 + lane;
     int b = slot >> 4;
     int c = (slot & 15) ^ (b & 7);
