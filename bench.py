@@ -293,6 +293,13 @@ def bench_embedding(cr, torch, dev, dev_normal, time_ms, wl):
     out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
     l_ms = time_ms(lambda: cr.embedding_lookup(ids, qe, se, out=out), 5, 50)
     l_bytes = T * (4 + D + 4 + 2 * D)
+    # the device's plain copy rate (torch's 1 GiB device-to-device copy), the
+    # practical ceiling for a kernel that streams reads and writes
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    c_ms = time_ms(lambda: dst.copy_(src), 3, 20)
+    c_GBps = 2 * (1 << 30) / (c_ms * 1e-3) / 1e9
+    del src, dst
     r = {
         "embed_quant_us": round(q_ms * 1e3, 1),
         "embed_quant_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
@@ -300,9 +307,12 @@ def bench_embedding(cr, torch, dev, dev_normal, time_ms, wl):
         "embed_lookup_us": round(l_ms * 1e3, 1),
         "embed_lookup_GBps": round(l_bytes / (l_ms * 1e-3) / 1e9, 1),
         "embed_lookup_pct_hbm": round(100 * l_bytes / (l_ms * 1e-3) / 1e9 / 8000.0, 1),
+        "device_copy_GBps": round(c_GBps, 1),
+        "embed_quant_pct_copy": round(100 * q_bytes / (q_ms * 1e-3) / 1e9 / c_GBps, 1),
+        "embed_lookup_pct_copy": round(100 * l_bytes / (l_ms * 1e-3) / 1e9 / c_GBps, 1),
     }
     log(f"[bench] embedding quant {r['embed_quant_us']} us ({r['embed_quant_GBps']} GB/s), lookup "
-        f"{r['embed_lookup_us']} us ({r['embed_lookup_GBps']} GB/s)")
+        f"{r['embed_lookup_us']} us ({r['embed_lookup_GBps']} GB/s); device copy {r['device_copy_GBps']} GB/s")
     return r
 
 
