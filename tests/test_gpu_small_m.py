@@ -1,12 +1,14 @@
 """Text-encoder shapes: one caption at a time (small, ragged M) and skinny
 outputs (N = 32), as in the training guide's text-encoder quantization
 (section 7.1, text encoder bullet).  With few 256 x 256 output tiles the
-forward splits the contraction (split-K) into int32 partials that one more
-launch sums and dequantizes.
+forward either runs the few-row kernel (M <= 128, N = 2048..8192, K <= 8192:
+16 output columns per workgroup, the waves' int32 sums added in LDS) or
+splits the contraction (split-K) into int32 partials that one more launch sums
+and dequantizes.
 
-  * the split forward equals the one-pass stages (quantize_act + the int8 GEMM
-    with its dequantizing epilogue) bit for bit: integer partial sums are exact
-    and the epilogue's fp32 operations are the same;
+  * either forward equals the one-pass stages (quantize_act + the int8 GEMM
+    with its dequantizing epilogue) bit for bit: integer sums are exact and the
+    epilogue's fp32 operations are the same;
   * sampled rows match the oracle (1e-2 row tolerance; exact int32 sums).
 """
 import numpy as np
@@ -30,7 +32,8 @@ def cr():
     return cr
 
 
-SHAPES = [(1, 4096, 4096), (7, 4096, 4096), (77, 4096, 4096), (300, 4096, 4096),
+SHAPES = [(1, 4096, 4096), (7, 4096, 4096), (77, 4096, 4096), (128, 4096, 4096),
+          (33, 4096, 3000), (16, 8192, 2048), (100, 8192, 4096), (300, 4096, 4096),
           (77, 4096, 12288), (77, 12288, 4096), (77, 4096, 32), (4096, 4096, 32), (129, 512, 640)]
 
 

@@ -1,0 +1,134 @@
+// Forward int8 contraction for few activation rows (M <= 128): one caption of
+// the text encoder at a time, the training guide's text-encoder quantization
+// ("LoRA Training Guide for MOSS-Image", section 7.1, text encoder bullet).
+//
+// y[m][n] = bf16( fl32( fl32( float(acc[m][n]) * s_x[m] ) * s_w[n] ) (+ bias[n]) ),
+// acc[m][n] = sum_k q_x[m][k] q_w[n][k]: the same int32 sums and the same fp32
+// epilogue operations as the tiled GEMM, so the output is identical to it.
+//
+// With 256 x 256 output tiles a caption fills a handful of CUs; here a
+// workgroup owns 16 output columns (16 rows of q_w, read exactly once) and all
+// M rows of q_x, which stay in L2 and are re-read by every workgroup.  The 8
+// waves split K in 64-wide steps (v_mfma_i32_16x16x64_i8: q_x's rows are the A
+// operand, 16 per tile, q_w's the B operand); lane group g = lane / 16 loads
+// bytes 16 g .. 16 g + 15 of a step for both operands, the same permutation of
+// k on both sides.  A wave issues all loads of a group of steps before
+// multiplying, and the 8 waves add their int32 tiles into LDS with integer
+// atomics (exact, so the order does not matter).
+#pragma clang fp contract(off)
+
+#include "common.h"
+#include "kernels.h"
+
+namespace convrot {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kSmWaves = 8;
+
+// T: 16-row tiles of q_x (M <= 16 T); G: 64-wide k-steps per load group.
+template <int T, int G>
+__global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_kernel(
+    const int8_t* __restrict__ qx, const float* __restrict__ sx, const int8_t* __restrict__ qw,
+    const float* __restrict__ sw, const uint16_t* __restrict__ bias, int64_t M, int64_t N,
+    int64_t K, uint16_t* __restrict__ y) {
+  __shared__ int32_t part[T][4][64];  // the waves' int32 sums (LDS integer adds)
+  for (int i = threadIdx.x; i < T * 256; i += 64 * kSmWaves) (&part[0][0][0])[i] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n = n0 + r < N ? n0 + r : N - 1;  // columns past the end reload the last one
+  const int8_t* wrow = qw + n * K + 16 * g;
+  const int8_t* xrow[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int64_t m = 16 * t + r < M ? 16 * t + r : M - 1;
+    xrow[t] = qx + m * K + 16 * g;
+  }
+  const int nks = (int)(K / 64);
+  const int nj = nks > wave ? (nks - wave + kSmWaves - 1) / kSmWaves : 0;  // this wave's steps
+  v4i acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = v4i{0, 0, 0, 0};
+  for (int j0 = 0; j0 < nj; j0 += G) {
+    uint4 wv[G], xv[G][T];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int j = j0 + u < nj ? j0 + u : nj - 1;  // past the wave's last step: reload it
+      const int64_t kb = (int64_t)(wave + kSmWaves * j) * 64;
+      wv[u] = *reinterpret_cast<const uint4*>(wrow + kb);
+#pragma unroll
+      for (int t = 0; t < T; ++t) xv[u][t] = *reinterpret_cast<const uint4*>(xrow[t] + kb);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the group ahead of the multiplies
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const uint4 w = j0 + u < nj ? wv[u] : make_uint4(0, 0, 0, 0);  // reloaded steps add 0
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xv[u][t]),
+                                                       __builtin_bit_cast(v4i, w), acc[t], 0, 0, 0);
+    }
+  }
+  // lane l holds rows 4 (l / 16) + v of tile t, column l % 16
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) atomicAdd(&part[t][v][lane], acc[t][v]);
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < T * 256; idx += 64 * kSmWaves) {
+    const int l = idx & 63, v = (idx >> 6) & 3, t = idx >> 8;
+    const int64_t m = 16 * t + 4 * (l >> 4) + v;
+    const int64_t nn = n0 + (l & 15);
+    if (m < M && nn < N) {
+      float f = (float)part[t][v][l];
+      f = f * sx[m];
+      f = f * sw[nn];
+      if (bias) f = f + __uint_as_float((uint32_t)bias[nn] << 16);
+      y[m * N + nn] = (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu);
+    }
+  }
+}
+
+template <int T>
+hipError_t launch_t(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw,
+                    const uint16_t* bias, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                    hipStream_t stream) {
+  constexpr int G = T <= 4 ? 8 : 4;
+  const int64_t grid = (N + 15) / 16;
+  hipLaunchKernelGGL((gemm_small_m_kernel<T, G>), dim3((unsigned)grid), dim3(64 * kSmWaves), 0,
+                     stream, qx, sx, qw, sw, bias, M, N, K, y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool use_small_m(int64_t M, int64_t N, int64_t K) {
+  // Measured against split-K (forward, M = 1..128): faster for N = 2048..4096
+  // at K = 4096; with N >= 12288 the per-workgroup re-reads of q_x (768
+  // workgroups) and with K = 12288 the 8-way K split per workgroup lose.
+  return M >= 1 && M <= kSmallM && K % 64 == 0 && K <= 8192 && N >= 2048 && N <= 8192;
+}
+
+hipError_t launch_gemm_small_m(const int8_t* qx, const float* sx, const int8_t* qw,
+                               const float* sw, const uint16_t* bias, int64_t M, int64_t N,
+                               int64_t K, uint16_t* y, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (M > kSmallM || K % 64 || K / 64 > 0x7fffffff || (N + 15) / 16 > 0x7fffffff)
+    return hipErrorInvalidValue;
+  switch ((M + 15) / 16) {
+    case 1: return launch_t<1>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+    case 2: return launch_t<2>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+    case 3: return launch_t<3>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+    case 4: return launch_t<4>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+    case 5: return launch_t<5>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+    case 6: return launch_t<6>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+    case 7: return launch_t<7>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+    default: return launch_t<8>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+  }
+}
+
+}  // namespace convrot
