@@ -164,6 +164,15 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// 4-byte direct global->LDS load (lane i's word lands at lds_base + 4 i); the
+// same ordering rules as dma16.
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+
 // 16-byte direct global->LDS load: lane i's 16 bytes land at lds_base + 16*i.
 __device__ __forceinline__ void load_lds_16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);

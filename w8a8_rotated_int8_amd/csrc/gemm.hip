@@ -234,9 +234,37 @@ __device__ __forceinline__ void dequant4(float v[4], float sjv, const float* si,
   }
 }
 
+// dequant4 with the tile's 256 s_i values staged in LDS (si_tile[i - i0]):
+// the same operations in the same order.
+__device__ __forceinline__ void dequant4_tile(float v[4], float sjv, const float* si_tile,
+                                              const uint16_t* bias, int64_t i, int64_t i0,
+                                              int64_t I) {
+#pragma clang fp contract(off)
+  if (i + 4 <= I) {
+    const float4 s4 = *reinterpret_cast<const float4*>(si_tile + (i - i0));
+    v[0] = v[0] * sjv * s4.x;
+    v[1] = v[1] * sjv * s4.y;
+    v[2] = v[2] * sjv * s4.z;
+    v[3] = v[3] * sjv * s4.w;
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t iu = i + u < I ? i + u : I - 1;
+      v[u] = v[u] * sjv * si_tile[iu - i0];
+    }
+  }
+  if (bias) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t iu = i + u < I ? i + u : I - 1;
+      v[u] = v[u] + __uint_as_float((uint32_t)bias[iu] << 16);
+    }
+  }
+}
+
 // One 256 x 256 output tile; every thread of the workgroup takes part.  LDS at
 // `lds`: the operand ring (STAGES * 2 * 256 * BK bytes), plus 32 KB for the
-// LoRA epilogue.
+// LoRA epilogue or 1 KB for the tile's s_i values of the dequantizing one.
 template <int EPI, bool PT, bool BF16, int WI, int WJ, int BK, int STAGES>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8_t* lds) {
   typedef typename AccT<BF16>::type acc_t;
@@ -259,6 +287,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
   const int64_t i0 = (int64_t)ti * kTile;
   const int64_t j0 = (int64_t)tj * kTile;
   const int nk = (int)(a.Kc * esz / BK);
+  // Dequantizing epilogues read s_j and s_i.  Loaded there, after the main
+  // loop, their latency sat in front of every store (~3 us per 4096^3
+  // launch); s_j is loaded into registers now and the dequantizing kernel's
+  // 256 s_i values are copied to LDS together with the first stage.
+  constexpr bool kScales = EPI == kEpiDequantBf16 || EPI == kEpiDequantLoraBf16;
+  constexpr bool kTileScales = EPI == kEpiDequantBf16 && !PT;
+  const float* const si_tile = reinterpret_cast<const float*>(lds + STAGES * 2 * kTile * BK);
+  float sj_pre[NJ];
+#pragma unroll
+  for (int y = 0; y < NJ; ++y) {
+    const int64_t j = j0 + wj * TJ + y * 32 + (lane & 31);
+    sj_pre[y] = kScales && j < a.J ? a.sj[j] : 0.f;
+  }
   // LoRA epilogue: the tile's 256 rows of lora_b (i) and lora_xa (j), R bf16
   // each, are copied to LDS past the operand ring now, long before the
   // epilogue reads them as MFMA fragments.
@@ -377,6 +418,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
       for (int t = 0; t < NJ; ++t)
         f[NI + t] = *reinterpret_cast<const uint4*>(qs + lds_off<BK>(wj * TJ + t * 32 + (lane & 31), chunk));
     };
+    if constexpr (kTileScales) {
+      // older than the stage loads, so complete once stage 0 is, and published
+      // by the same barrier
+      if (wave < kTile / 64) {
+        const int64_t i = i0 + wave * 64 + lane;
+        dma4(static_cast<const float*>(a.si) + (i < a.I ? i : a.I - 1),
+             lds_u32(si_tile) + wave * 256);
+      }
+    }
     // all STAGES buffers start filled; the buffer of stage kt is refilled with
     // stage kt + STAGES at the end of stage kt
 #pragma unroll
@@ -490,6 +540,33 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
       const int pos = (il >> 3) ^ (jl & kChunkMask);
       *reinterpret_cast<uint2*>(stg + jl * kRowBytes + pos * 16 + (il & 7) * 2) = make_uint2(lo, hi);
     };
+    // Write the staged rows 32 y0 .. 32 (y0 + ny) - 1 of this wave's sub-tile:
+    // 16-byte chunks of contiguous output rows, 64 lanes per step.  The plain
+    // dequantizing epilogue calls it after each y, so the stores of one slice
+    // are in flight while the next is converted.
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+    auto flush = [&](int y0, int ny) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes landed
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+      const int kChunks = 32 * ny * (TI / 8);
+#pragma unroll 4
+      for (int c0 = 0; c0 < kChunks; c0 += 64) {
+        const int idx = c0 + lane;
+        const int jl = 32 * y0 + idx / (TI / 8), c = idx % (TI / 8);
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + jl * kRowBytes + ((c ^ (jl & kChunkMask)) * 16));
+        const int64_t j = j0 + wj * TJ + jl;
+        const int64_t i = i0 + wi * TI + 8 * c;
+        if (j >= a.J || i >= a.I) continue;
+        uint16_t* dst = out + j * a.ldo + i;
+        if (i + 8 <= a.I) {
+          *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+          const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+          for (int u = 0; u < 8 && i + u < a.I; ++u) dst[u] = (uint16_t)(wds[u >> 1] >> (16 * (u & 1)));
+        }
+      }
+    };
     if constexpr (EPI == kEpiInvRotBf16) {
       static_assert(TI == 128, "one wave owns whole 128-blocks along i");
 #pragma unroll
@@ -533,6 +610,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
           }
         }
       }
+      flush(0, NJ);
     } else {
       constexpr bool kDequant = EPI == kEpiDequantBf16 || EPI == kEpiDequantLoraBf16;
       constexpr bool kLora = EPI == kEpiDequantLoraBf16;
@@ -549,7 +627,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
         const int jl = y * 32 + (lane & 31);
         const int64_t j = j0 + wj * TJ + jl;
         float sjv = 1.f;
-        if constexpr (kDequant) sjv = j < a.J ? a.sj[j] : 0.f;
+        if constexpr (kDequant) sjv = sj_pre[y];
 #pragma unroll
         for (int x = 0; x < NI; ++x) {
           v16f lo = {};
@@ -565,7 +643,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
             float v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) v[u] = (float)acc[x][y][4 * g + u];
-            if constexpr (kDequant) dequant4(v, sjv, a.si, a.bias, i, a.I);
+            if constexpr (kTileScales) dequant4_tile(v, sjv, si_tile, a.bias, i, i0, a.I);
+            else if constexpr (kDequant) dequant4(v, sjv, a.si, a.bias, i, a.I);
             if constexpr (kLora) {
 #pragma unroll
               for (int u = 0; u < 4; ++u) v[u] = v[u] + a.lora_scale * lo[4 * g + u];
@@ -573,29 +652,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
             put8(jl, il, pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
           }
         }
+        if constexpr (!kLora) flush(y, 1);
       }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes landed
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("" ::: "memory");
-    // read back: TJ rows x (TI / 8) chunks of 16 bytes, 64 lanes per step
-    uint16_t* out = static_cast<uint16_t*>(a.out);
-    constexpr int kChunks = TJ * (TI / 8);
-#pragma unroll
-    for (int c0 = 0; c0 < kChunks; c0 += 64) {
-      const int idx = c0 + lane;
-      const int jl = idx / (TI / 8), c = idx % (TI / 8);
-      const uint4 v = *reinterpret_cast<const uint4*>(stg + jl * kRowBytes + ((c ^ (jl & kChunkMask)) * 16));
-      const int64_t j = j0 + wj * TJ + jl;
-      const int64_t i = i0 + wi * TI + 8 * c;
-      if (j >= a.J || i >= a.I) continue;
-      uint16_t* dst = out + j * a.ldo + i;
-      if (i + 8 <= a.I) {
-        *reinterpret_cast<uint4*>(dst) = v;
-      } else {
-        const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
-        for (int u = 0; u < 8 && i + u < a.I; ++u) dst[u] = (uint16_t)(wds[u >> 1] >> (16 * (u & 1)));
-      }
+      if constexpr (kLora) flush(0, NJ);
     }
   }
 }
@@ -652,7 +711,8 @@ __global__ __launch_bounds__(256) void splitk_dequant_kernel(const int32_t* __re
 template <int EPI, bool PT, bool BF16, int WI, int WJ, int BK, int STAGES>
 hipError_t launch(const GemmArgs& a, hipStream_t stream) {
   // operand ring, plus the LoRA rows of one tile (2 x 256 rows x up to 32 bf16)
-  constexpr int kLds = STAGES * 2 * kTile * BK + (EPI == kEpiDequantLoraBf16 ? 2 * kTile * 64 : 0);
+  constexpr int kLds = STAGES * 2 * kTile * BK + (EPI == kEpiDequantLoraBf16 ? 2 * kTile * 64 : 0) +
+                       (EPI == kEpiDequantBf16 && !PT ? kTile * 4 : 0);
   auto kern = gemm_kernel<EPI, PT, BF16, WI, WJ, BK, STAGES>;
   static bool configured = false;
   if (!configured) {
