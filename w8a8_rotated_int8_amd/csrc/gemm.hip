@@ -291,7 +291,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
   // loop, their latency sat in front of every store (~3 us per 4096^3
   // launch); s_j is loaded into registers now and the dequantizing kernel's
   // 256 s_i values are copied to LDS together with the first stage.
-  constexpr bool kScales = EPI == kEpiDequantBf16 || EPI == kEpiDequantLoraBf16;
+  constexpr bool kScales =
+      EPI == kEpiDequantBf16 || EPI == kEpiDequantLoraBf16 || EPI == kEpiInvRotBf16;
   constexpr bool kTileScales = EPI == kEpiDequantBf16 && !PT;
   const float* const si_tile = reinterpret_cast<const float*>(lds + STAGES * 2 * kTile * BK);
   float sj_pre[NJ];
@@ -573,7 +574,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
       for (int y = 0; y < NJ; ++y) {
         const int jl = y * 32 + (lane & 31);
         const int64_t j = j0 + wj * TJ + jl;
-        const float sjv = j < a.J ? a.sj[j] : 0.f;
+        const float sjv = sj_pre[y];
         float w[64];
 #pragma unroll
         for (int x = 0; x < 4; ++x)
