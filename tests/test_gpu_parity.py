@@ -207,6 +207,21 @@ def test_linear_fwd_attn_full_size(cr, orc):
 # Input gradients
 # --------------------------------------------------------------------------
 
+@pytest.mark.parametrize("M,N", [(33, 256), (17, 1152), (9, 2048), (7, 4224), (5, 16384),
+                                 (3, 24576), (3, 24704), (2, 32768)])
+def test_bwd_quant_dy_exact(cr, orc, M, N):
+    # the dY quantizer on every row plan: packed short rows, slices with the
+    # column scales staged in LDS (up to 12 slices), and longer rows that read
+    # them from global memory
+    say(f"bwd_quant_dy M={M} N={N}")
+    dy = wl.normal_bf16((M, N), 1e-3, 11, N % 1000)
+    sw = (np.random.default_rng(N).random(N) * 1e-3 + 1e-5).astype(np.float32)
+    qg, sg = cr.bwd_quant_dy(bf16_to_dev(dy), torch.from_numpy(sw).cuda())
+    oqg, osg = orc.bwd_quant_dy(dy, sw)
+    assert_exact(host(sg), osg, "s_g")
+    assert_exact(host(qg), oqg, "q_g")
+
+
 def _bwd_int8(cr, orc, dy, w, rows=None):
     qw, sw = cr.quantize_weight(bf16_to_dev(w))
     oqw, osw, _ = orc.rotate_quantize(w)

@@ -63,13 +63,14 @@ __device__ __forceinline__ void swap_rows16(double& vdst, double& src0) {
 // register bit 4 with a lane bit, so that the butterfly partners meet in one
 // lane.  After both, lane quarter q = L >> 4 holds outputs 16 q + e in v[e]
 // and 64 + 16 q + e in v[e + 16] (e < 16).
-template <int MODE, int SB = kSpanBlocks>
+template <int MODE, int SB = kSpanBlocks, bool CSL = false>
 __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_blocks, int nb,
                                               int64_t span_elem0, int blk_in_row0, int64_t row0,
                                               int waves_per_row, int8_t* __restrict__ q,
                                               float* __restrict__ scale,
                                               const float* __restrict__ colscale,
-                                              float* seg_max_wave, float* row_part_max) {
+                                              float* seg_max_wave, float* row_part_max,
+                                              const uint8_t* cs_lds = nullptr) {
 #pragma clang fp contract(off)
   static_assert(SB == 16 || SB == 32, "a span is one or two passes of 16 blocks");
   constexpr int NP = SB / 16;  // passes
@@ -140,16 +141,24 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
 #pragma unroll
       for (int e = 0; e < 32; ++e) r[k][e] = (float)(v[e] * kInvSqrt128);
     } else {
-      // fold the per-column scale: element 32 g + e of block b
+      // fold the per-column scale: element 32 g + e of block b.  With CSL the
+      // span's scales were staged at cs_lds by stage_colscale (chunk c of block b
+      // at b * 32 + (c ^ (b & 15))); otherwise they are read from global memory.
       const int64_t col0 =
           active ? (int64_t)(blk_in_row0 + (waves_per_row == 1 ? b % nb : b)) * kBlock + 32 * g
                  : 0;
       const float4* cs = reinterpret_cast<const float4*>(colscale + col0);
+      auto scale4 = [&](int i2) {  // floats 32 g + 4 i2 .. + 3 of block b
+        if constexpr (CSL)
+          return *reinterpret_cast<const float4*>(cs_lds + b * 512 + 16 * ((8 * g + i2) ^ (b & 15)));
+        else
+          return active ? cs[i2] : make_float4(0.f, 0.f, 0.f, 0.f);
+      };
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-        float4 s0 = active ? cs[2 * i] : make_float4(0.f, 0.f, 0.f, 0.f);
-        float4 s1 = active ? cs[2 * i + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 s0 = scale4(2 * i);
+        float4 s1 = scale4(2 * i + 1);
         float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -282,6 +291,29 @@ __device__ __forceinline__ void stage_span(const uint16_t* __restrict__ x, int64
     int c = (slot & 15) ^ (b & 7);
     if (b >= span_blocks) { b = span_blocks - 1; c = 15; }
     dma16(x + span_elem0 + (int64_t)b * kBlock + c * 8, base + i * 1024);
+  }
+}
+
+// Fold mode: copy the per-column scales of a span's blocks (128 floats, 32
+// chunks of 16 bytes per block) to LDS with coalesced direct loads, SB / 2 per
+// lane.  Chunk c of span block b lands at b * 32 + (c ^ (b & 15)): the fold
+// pass reads chunk 8 g + i of block p in lanes 16 g + p, and the XOR spreads
+// those 16 lanes over 16 different bank groups.  Blocks past the span reload
+// a chunk of its last block (never read).
+template <int SB>
+__device__ __forceinline__ void stage_colscale(const float* __restrict__ colscale, int span_blocks,
+                                               int nb, int blk_in_row0, int waves_per_row,
+                                               uint8_t* cs_lds) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_u32(cs_lds));
+#pragma unroll
+  for (int i = 0; i < SB / 2; ++i) {
+    const int slot = i * 64 + lane;
+    int b = slot >> 5;
+    int c = (slot & 31) ^ (b & 15);
+    if (b >= span_blocks) { b = span_blocks - 1; c = 0; }
+    const int gb = blk_in_row0 + (waves_per_row == 1 ? b % nb : b);
+    dma16(colscale + (int64_t)gb * kBlock + 4 * c, base + i * 1024);
   }
 }
 
