@@ -169,6 +169,30 @@ __device__ __forceinline__ void load_transposed(const int8_t* src, int64_t ld, i
   for (int r = 0; r < 16; ++r) t.r[r] = *reinterpret_cast<const uint2*>(p + r * ld);
 }
 
+// Half `hf` of store_transposed: columns i = 8 ic + 4 hf .. + 3 (the .x or .y
+// bytes of the loaded rows): 32 v_perm and 4 LDS writes.
+__device__ __forceinline__ void store_transposed_half(const TransposedRegs& t, uint8_t* lds_stage,
+                                                      int tid, int hf) {
+  const int lane = tid & 63, wave = tid >> 6;
+  int ic = lane & 31;
+  int kg = (lane >> 5) + 2 * wave;
+  uint32_t o[4][4];  // o[j][d]: bytes (k = 4d .. 4d+3) of column i = 8 ic + 4 hf + j
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    if (hf == 0)
+      transpose4x4(t.r[4 * d].x, t.r[4 * d + 1].x, t.r[4 * d + 2].x, t.r[4 * d + 3].x, o[0][d],
+                   o[1][d], o[2][d], o[3][d]);
+    else
+      transpose4x4(t.r[4 * d].y, t.r[4 * d + 1].y, t.r[4 * d + 2].y, t.r[4 * d + 3].y, o[0][d],
+                   o[1][d], o[2][d], o[3][d]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    *reinterpret_cast<uint4*>(lds_stage + lds_off<128>(8 * ic + 4 * hf + j, kg)) =
+        make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]);
+  }
+}
+
 __device__ __forceinline__ void store_transposed(const TransposedRegs& t, uint8_t* lds_stage,
                                                  int tid) {
   const int lane = tid & 63, wave = tid >> 6;
@@ -358,25 +382,115 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
   };
 
   if constexpr (PT) {
+    // Transposed P (the int8 input gradient): P's stage block arrives in
+    // registers one stage ahead (16 eight-byte loads per thread) and is
+    // transposed into LDS in two halves, each interleaved with the MFMAs of one
+    // slice of the current stage; Q arrives by direct loads.  As in the
+    // row-major case, the fragment reads of slice s + 1 are interleaved with
+    // the MFMAs of slice s, and the last stage is peeled.
+    static_assert(BK / 32 == 4, "transposed P: 4 slices per stage");
+    constexpr int kQLoads = kTile * (BK / 16) / NT;  // Q direct loads per thread per stage
+    const int8_t* Pt = static_cast<const int8_t*>(a.P);
     TransposedRegs tr;
-    stage_rows<BK, NT>(Q, a.ldq * esz, j0, a.J, 0, Qs(0), tid);
-    load_transposed(static_cast<const int8_t*>(a.P), a.ldp, a.I, i0, 0, tid, tr);
-    store_transposed(tr, Ps(0), tid);
-    int buf = 0;
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_vm<0>();
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
-      raw_barrier();
-      const bool more = kt + 1 < nk;
-      if (more) {
-        const int64_t kb = (int64_t)(kt + 1) * BK;
-        load_transposed(static_cast<const int8_t*>(a.P), a.ldp, a.I, i0, kb, tid, tr);
-        stage_rows<BK, NT>(Q, a.ldq * esz, j0, a.J, kb, Qs(buf ^ 1), tid);
+    uint4 F[2][NI + NJ];
+    auto read_frags = [&](int buf, int s, uint4* f) {
+      const uint8_t* ps = Ps(buf);
+      const uint8_t* qs = Qs(buf);
+      const int chunk = 2 * s + (lane >> 5);
+#pragma unroll
+      for (int t = 0; t < NI; ++t)
+        f[t] = *reinterpret_cast<const uint4*>(ps + lds_off<BK>(wi * TI + t * 32 + (lane & 31), chunk));
+#pragma unroll
+      for (int t = 0; t < NJ; ++t)
+        f[NI + t] = *reinterpret_cast<const uint4*>(qs + lds_off<BK>(wj * TJ + t * 32 + (lane & 31), chunk));
+    };
+    // MFMAs of slice s; the next slice's fragment reads (issued just before)
+    // go one per MFMA, then NV VALU operations and ND LDS writes of a transpose
+    // half are spread over the remaining MFMAs.
+    auto mfma_slice = [&](int s, auto nv, auto nd) {
+      constexpr int NV = decltype(nv)::value, ND = decltype(nd)::value;
+#pragma unroll
+      for (int x = 0; x < NI; ++x)
+#pragma unroll
+        for (int y = 0; y < NJ; ++y) acc[x][y] = mfma(F[s & 1][x], F[s & 1][NI + y], acc[x][y]);
+#pragma unroll
+      for (int i = 0; i < NI + NJ; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       }
-      compute_stage(buf);
-      if (more) store_transposed(tr, Ps(buf ^ 1), tid);
-      buf ^= 1;
+      constexpr int rest = NI * NJ - (NI + NJ);
+      if constexpr (NV > 0) {
+#pragma unroll
+        for (int i = 0; i < rest; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, NV / rest, 0);  // a few VALU
+          if (i % (rest / ND) == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, rest, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using Z = std::integral_constant<int, 0>;
+    using V32 = std::integral_constant<int, 32>;
+    using D4 = std::integral_constant<int, 4>;
+
+    stage_rows<BK, NT>(Q, a.ldq * esz, j0, a.J, 0, Qs(0), tid);
+    load_transposed(Pt, a.ldp, a.I, i0, 0, tid, tr);
+    store_transposed(tr, Ps(0), tid);
+    if (nk > 1) {
+      stage_rows<BK, NT>(Q, a.ldq * esz, j0, a.J, BK, Qs(1), tid);
+      load_transposed(Pt, a.ldp, a.I, i0, BK, tid, tr);
+      wait_vm<kQLoads + 16>();  // stage 0's Q loads (the oldest) have landed
+    } else {
+      wait_vm<0>();
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's P writes landed
+    raw_barrier();
+    read_frags(0, 0, F[0]);
+    auto stage = [&](int kt, auto has_next) {
+      constexpr bool HAS_NEXT = decltype(has_next)::value;
+      const int buf = kt & 1;
+      // slice 0
+      read_frags(buf, 1, F[1]);
+      mfma_slice(0, Z{}, Z{});
+      // slices 1 and 2: transpose the next stage's P into the other buffer
+      read_frags(buf, 2, F[0]);
+      if constexpr (HAS_NEXT) {
+        store_transposed_half(tr, Ps(buf ^ 1), tid, 0);
+        mfma_slice(1, V32{}, D4{});
+      } else {
+        mfma_slice(1, Z{}, Z{});
+      }
+      read_frags(buf, 3, F[1]);
+      if constexpr (HAS_NEXT) {
+        store_transposed_half(tr, Ps(buf ^ 1), tid, 1);
+        mfma_slice(2, V32{}, D4{});
+        // publish stage kt + 1: its Q loads have landed and every wave's P
+        // writes are done; then start stage kt + 2's loads
+        wait_vm<0>();
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        raw_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(buf ^ 1, 0, F[0]);
+        mfma_slice(3, Z{}, Z{});
+        if (kt + 2 < nk) {
+          const int64_t kb = (int64_t)(kt + 2) * BK;
+          stage_rows<BK, NT>(Q, a.ldq * esz, j0, a.J, kb, Qs(buf), tid);
+          load_transposed(Pt, a.ldp, a.I, i0, kb, tid, tr);
+        }
+      } else {
+        mfma_slice(2, Z{}, Z{});
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int x = 0; x < NI; ++x)
+#pragma unroll
+          for (int y = 0; y < NJ; ++y) acc[x][y] = mfma(F[1][x], F[1][NI + y], acc[x][y]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, std::true_type{});
+    if (nk > 0) stage(nk - 1, std::false_type{});
   } else {
     // Per-thread source pointers and LDS destinations of the stage loads,
     // computed once: a stage load is then one 64-bit add per instruction.
