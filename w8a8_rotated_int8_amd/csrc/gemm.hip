@@ -148,37 +148,41 @@ __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c,
   o3 = __builtin_amdgcn_perm(u1, t1, 0x07060302u);         // a3 b3 c3 d3
 }
 
-// Transposed int8 operand (BK = 128, 256 threads): source [Kc, I] (I
-// contiguous).  Each lane loads a 16 (k) x 8 (i) byte block with 8-byte loads
-// (32 lanes cover the 256 i of the tile in one row), transposes it in
-// registers and writes 8 LDS rows (one per i) of 16 k-bytes each.
+// Transposed int8 operand (BK = 128): source [Kc, I] (I contiguous).  The
+// NT / 32 groups of 32 lanes split the stage's 128 k rows, RP = 4096 / NT rows
+// each; lane ic of a group loads an RP (k) x 8 (i) byte block with 8-byte
+// loads (32 lanes cover the 256 i of the tile), transposes it in registers
+// (v_perm) and writes 8 LDS rows (one per i) of RP k-bytes each.
+template <int NT>
 struct TransposedRegs {
-  uint2 r[16];
+  static constexpr int RP = 128 * 32 / NT;
+  uint2 r[RP];
 };
 
+template <int NT>
 __device__ __forceinline__ void load_transposed(const int8_t* src, int64_t ld, int64_t I,
                                                 int64_t i0, int64_t k0, int tid,
-                                                TransposedRegs& t) {
-  const int lane = tid & 63, wave = tid >> 6;
-  int ic = lane & 31;
-  int kg = (lane >> 5) + 2 * wave;
+                                                TransposedRegs<NT>& t) {
+  constexpr int RP = TransposedRegs<NT>::RP;
+  const int ic = tid & 31, kg = tid >> 5;
   int64_t i = i0 + 8 * ic;
   i = i + 8 <= I ? i : I - 8;
-  const int8_t* p = src + (k0 + 16 * kg) * ld + i;
+  const int8_t* p = src + (k0 + RP * kg) * ld + i;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) t.r[r] = *reinterpret_cast<const uint2*>(p + r * ld);
+  for (int r = 0; r < RP; ++r) t.r[r] = *reinterpret_cast<const uint2*>(p + r * ld);
 }
 
-// Half `hf` of store_transposed: columns i = 8 ic + 4 hf .. + 3 (the .x or .y
-// bytes of the loaded rows): 32 v_perm and 4 LDS writes.
-__device__ __forceinline__ void store_transposed_half(const TransposedRegs& t, uint8_t* lds_stage,
-                                                      int tid, int hf) {
-  const int lane = tid & 63, wave = tid >> 6;
-  int ic = lane & 31;
-  int kg = (lane >> 5) + 2 * wave;
-  uint32_t o[4][4];  // o[j][d]: bytes (k = 4d .. 4d+3) of column i = 8 ic + 4 hf + j
+// Half `hf` of the transposed write: columns i = 8 ic + 4 hf .. + 3 (the .x
+// or .y bytes of the loaded rows).
+template <int NT>
+__device__ __forceinline__ void store_transposed_half(const TransposedRegs<NT>& t,
+                                                      uint8_t* lds_stage, int tid, int hf) {
+  constexpr int RP = TransposedRegs<NT>::RP;
+  static_assert(RP == 8 || RP == 16, "8 or 16 k rows per lane");
+  const int ic = tid & 31, kg = tid >> 5;
+  uint32_t o[4][RP / 4];  // o[j][d]: bytes (k = 4d .. 4d+3 of the lane's rows) of column 8 ic + 4 hf + j
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
+  for (int d = 0; d < RP / 4; ++d) {
     if (hf == 0)
       transpose4x4(t.r[4 * d].x, t.r[4 * d + 1].x, t.r[4 * d + 2].x, t.r[4 * d + 3].x, o[0][d],
                    o[1][d], o[2][d], o[3][d]);
@@ -188,29 +192,19 @@ __device__ __forceinline__ void store_transposed_half(const TransposedRegs& t, u
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    *reinterpret_cast<uint4*>(lds_stage + lds_off<128>(8 * ic + 4 * hf + j, kg)) =
-        make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]);
+    uint8_t* dst = lds_stage + lds_off<128>(8 * ic + 4 * hf + j, (RP * kg) >> 4) + ((RP * kg) & 15);
+    if constexpr (RP == 16)
+      *reinterpret_cast<uint4*>(dst) = make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]);
+    else
+      *reinterpret_cast<uint2*>(dst) = make_uint2(o[j][0], o[j][1]);
   }
 }
 
-__device__ __forceinline__ void store_transposed(const TransposedRegs& t, uint8_t* lds_stage,
+template <int NT>
+__device__ __forceinline__ void store_transposed(const TransposedRegs<NT>& t, uint8_t* lds_stage,
                                                  int tid) {
-  const int lane = tid & 63, wave = tid >> 6;
-  int ic = lane & 31;
-  int kg = (lane >> 5) + 2 * wave;
-  uint32_t o[8][4];  // o[j][d]: bytes (k = 4d .. 4d+3) of column i = 8 ic + j
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    transpose4x4(t.r[4 * d].x, t.r[4 * d + 1].x, t.r[4 * d + 2].x, t.r[4 * d + 3].x, o[0][d],
-                 o[1][d], o[2][d], o[3][d]);
-    transpose4x4(t.r[4 * d].y, t.r[4 * d + 1].y, t.r[4 * d + 2].y, t.r[4 * d + 3].y, o[4][d],
-                 o[5][d], o[6][d], o[7][d]);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    *reinterpret_cast<uint4*>(lds_stage + lds_off<128>(8 * ic + j, kg)) =
-        make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]);
-  }
+  store_transposed_half<NT>(t, lds_stage, tid, 0);
+  store_transposed_half<NT>(t, lds_stage, tid, 1);
 }
 
 // Dispatch id -> (i tile, j tile), XCD-aware (see the file comment).
@@ -298,7 +292,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
   constexpr int NI = TI / 32, NJ = TJ / 32;        // MFMA tiles per wave
   constexpr int kStage = kTile * BK;               // bytes per operand per stage
   constexpr int kLoadsPerStage = 2 * kTile * (BK / 16) / NT;  // DMA per thread per stage
-  static_assert(!PT || (BK == 128 && NT == 256 && STAGES == 2), "transposed P: BK 128, 4 waves");
+  static_assert(!PT || (BK == 128 && (NT == 256 || NT == 512) && STAGES == 2),
+                "transposed P: BK 128, 4 or 8 waves, 2 stages");
   static_assert(EPI != kEpiInvRotBf16 || TI == 128, "inverse rotation needs 128-wide wave tiles");
 
   const int tid = threadIdx.x;
@@ -391,7 +386,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
     static_assert(BK / 32 == 4, "transposed P: 4 slices per stage");
     constexpr int kQLoads = kTile * (BK / 16) / NT;  // Q direct loads per thread per stage
     const int8_t* Pt = static_cast<const int8_t*>(a.P);
-    TransposedRegs tr;
+    TransposedRegs<NT> tr;
     uint4 F[2][NI + NJ];
     auto read_frags = [&](int buf, int s, uint4* f) {
       const uint8_t* ps = Ps(buf);
@@ -404,44 +399,37 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
       for (int t = 0; t < NJ; ++t)
         f[NI + t] = *reinterpret_cast<const uint4*>(qs + lds_off<BK>(wj * TJ + t * 32 + (lane & 31), chunk));
     };
-    // MFMAs of slice s; the next slice's fragment reads (issued just before)
-    // go one per MFMA, then NV VALU operations and ND LDS writes of a transpose
-    // half are spread over the remaining MFMAs.
+    // MFMAs of slice s with, spread over them: the next slice's fragment
+    // reads (issued just before, one per MFMA from the first), NV VALU
+    // operations (the transposes of a half, evenly) and ND LDS writes (its
+    // results, on the last MFMAs).
     auto mfma_slice = [&](int s, auto nv, auto nd) {
       constexpr int NV = decltype(nv)::value, ND = decltype(nd)::value;
+      constexpr int NM = NI * NJ;
 #pragma unroll
       for (int x = 0; x < NI; ++x)
 #pragma unroll
         for (int y = 0; y < NJ; ++y) acc[x][y] = mfma(F[s & 1][x], F[s & 1][NI + y], acc[x][y]);
 #pragma unroll
-      for (int i = 0; i < NI + NJ; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      }
-      constexpr int rest = NI * NJ - (NI + NJ);
-      if constexpr (NV > 0) {
-#pragma unroll
-        for (int i = 0; i < rest; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, NV / rest, 0);  // a few VALU
-          if (i % (rest / ND) == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
-        }
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, rest, 0);
+      for (int i = 0; i < NM; ++i) {
+        if (i < NI + NJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // one MFMA
+        if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV / NM, 0);  // VALU
+        if (ND > 0 && i >= NM - ND) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
       }
       __builtin_amdgcn_sched_barrier(0);
     };
     using Z = std::integral_constant<int, 0>;
-    using V32 = std::integral_constant<int, 32>;
-    using D4 = std::integral_constant<int, 4>;
+    using VH = std::integral_constant<int, 2 * TransposedRegs<NT>::RP>;  // v_perm per half
+    using D4 = std::integral_constant<int, 4>;                           // LDS writes per half
 
     stage_rows<BK, NT>(Q, a.ldq * esz, j0, a.J, 0, Qs(0), tid);
     load_transposed(Pt, a.ldp, a.I, i0, 0, tid, tr);
-    store_transposed(tr, Ps(0), tid);
+    store_transposed<NT>(tr, Ps(0), tid);
     if (nk > 1) {
       stage_rows<BK, NT>(Q, a.ldq * esz, j0, a.J, BK, Qs(1), tid);
       load_transposed(Pt, a.ldp, a.I, i0, BK, tid, tr);
-      wait_vm<kQLoads + 16>();  // stage 0's Q loads (the oldest) have landed
+      wait_vm<kQLoads + TransposedRegs<NT>::RP>();  // stage 0's Q loads (the oldest) have landed
     } else {
       wait_vm<0>();
     }
@@ -457,15 +445,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
       // slices 1 and 2: transpose the next stage's P into the other buffer
       read_frags(buf, 2, F[0]);
       if constexpr (HAS_NEXT) {
-        store_transposed_half(tr, Ps(buf ^ 1), tid, 0);
-        mfma_slice(1, V32{}, D4{});
+        store_transposed_half<NT>(tr, Ps(buf ^ 1), tid, 0);
+        mfma_slice(1, VH{}, D4{});
       } else {
         mfma_slice(1, Z{}, Z{});
       }
       read_frags(buf, 3, F[1]);
       if constexpr (HAS_NEXT) {
-        store_transposed_half(tr, Ps(buf ^ 1), tid, 1);
-        mfma_slice(2, V32{}, D4{});
+        store_transposed_half<NT>(tr, Ps(buf ^ 1), tid, 1);
+        mfma_slice(2, VH{}, D4{});
         // publish stage kt + 1: its Q loads have landed and every wave's P
         // writes are done; then start stage kt + 2's loads
         wait_vm<0>();
