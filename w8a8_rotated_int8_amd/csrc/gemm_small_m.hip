@@ -93,12 +93,126 @@ __global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_kernel(
   }
 }
 
+// The same contraction with q_x staged through LDS.  K runs in chunks of 512
+// bytes; a chunk of all 16 T rows of q_x arrives by whole-line direct loads
+// (8 T instructions of 1 KB, T per wave) into one of two LDS buffers while the
+// previous chunk is multiplied, and wave w multiplies the chunk's 64-byte step
+// w.  Row r's 16-byte piece c sits at r * 512 + 16 (c ^ (r & 15)), so the 16
+// rows of one fragment read fall in different banks.  The waves' q_w steps of
+// every chunk (K <= 4096: at most 8 per wave) are loaded at the start with
+// loads the compiler does not track, so that its waits do not cover the
+// direct loads issued after them.
+constexpr int kSmChunk = 512;
+constexpr int kSmMaxChunks = 8;
+
+__device__ __forceinline__ uint4 load16_untracked(const void* p) {
+  uint4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+
+template <int T>
+__global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_lds_kernel(
+    const int8_t* __restrict__ qx, const float* __restrict__ sx, const int8_t* __restrict__ qw,
+    const float* __restrict__ sw, const uint16_t* __restrict__ bias, int64_t M, int64_t N,
+    int64_t K, uint16_t* __restrict__ y) {
+  extern __shared__ __align__(16) uint8_t xs[];  // two buffers of 16 T rows x 512 bytes
+  __shared__ int32_t part[T][4][64];
+  for (int i = threadIdx.x; i < T * 256; i += 64 * kSmWaves) (&part[0][0][0])[i] = 0;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n = n0 + r < N ? n0 + r : N - 1;  // columns past the end reload the last one
+  const int nch = (int)(K / kSmChunk);
+  uint4 wv[kSmMaxChunks];
+  {
+    const int8_t* wrow = qw + n * K + 64 * wave + 16 * g;
+#pragma unroll
+    for (int c = 0; c < kSmMaxChunks; ++c)  // past the last chunk: reload it (unused)
+      wv[c] = load16_untracked(wrow + (c < nch ? c : nch - 1) * kSmChunk);
+  }
+  constexpr int kBuf = 16 * T * kSmChunk;
+  const uint32_t xs_base = __builtin_amdgcn_readfirstlane(lds_u32(xs));
+  auto stage = [&](int c, int b) {
+#pragma unroll
+    for (int it = 0; it < T; ++it) {
+      const int inst = it * kSmWaves + wave;  // 1 KB piece of the chunk
+      const int slot = inst * 64 + lane;
+      const int row = slot >> 5;
+      const int pc = (slot & 31) ^ (row & 15);  // the 16-byte piece this lane fetches
+      const int64_t m = row < M ? row : M - 1;  // rows past the end reload the last one
+      dma16(qx + m * K + (int64_t)c * kSmChunk + 16 * pc, xs_base + b * kBuf + inst * 1024);
+    }
+  };
+  v4i acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = v4i{0, 0, 0, 0};
+  stage(0, 0);
+#pragma unroll
+  for (int c = 0; c < kSmMaxChunks; ++c) {
+    if (c >= nch) break;
+    wait_vm_n<0>();  // this wave's part of chunk c landed (and, older, its q_w loads)
+    if (c == 0) {
+#pragma unroll
+      for (int cc = 0; cc < kSmMaxChunks; ++cc)  // q_w values are used after the wait
+        asm volatile("" : "+v"(wv[cc].x), "+v"(wv[cc].y), "+v"(wv[cc].z), "+v"(wv[cc].w));
+    }
+    __syncthreads();  // every wave's part landed; every wave is done with chunk c - 1
+    if (c + 1 < nch) stage(c + 1, (c + 1) & 1);
+    const uint8_t* buf = xs + (c & 1) * kBuf;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int row = 16 * t + r;
+      const uint4 xf =
+          *reinterpret_cast<const uint4*>(buf + row * kSmChunk + 16 * ((4 * wave + g) ^ r));
+      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xf),
+                                                     __builtin_bit_cast(v4i, wv[c]), acc[t], 0,
+                                                     0, 0);
+    }
+  }
+  // lane l holds rows 4 (l / 16) + v of tile t, column l % 16
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) atomicAdd(&part[t][v][lane], acc[t][v]);
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < T * 256; idx += 64 * kSmWaves) {
+    const int l = idx & 63, v = (idx >> 6) & 3, t = idx >> 8;
+    const int64_t m = 16 * t + 4 * (l >> 4) + v;
+    const int64_t nn = n0 + (l & 15);
+    if (m < M && nn < N) {
+      float f = (float)part[t][v][l];
+      f = f * sx[m];
+      f = f * sw[nn];
+      if (bias) f = f + __uint_as_float((uint32_t)bias[nn] << 16);
+      y[m * N + nn] = (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu);
+    }
+  }
+}
+
 template <int T>
 hipError_t launch_t(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw,
                     const uint16_t* bias, int64_t M, int64_t N, int64_t K, uint16_t* y,
                     hipStream_t stream) {
-  constexpr int G = T <= 4 ? 8 : 4;
   const int64_t grid = (N + 15) / 16;
+  // Staging q_x pays from 3 row tiles on (measured, graph replays at K = 4096:
+  // M = 77 17.2 -> 14.2 us, M = 128 23.6 -> 17.6 us); at M <= 16 its chunk
+  // barriers cost more than the re-reads they save (7.9 -> 9.4 us at M = 1).
+  if (T >= 3 && K % kSmChunk == 0 && K / kSmChunk <= kSmMaxChunks) {
+    constexpr int kLds = 2 * 16 * T * kSmChunk;
+    static bool configured = false;
+    if (!configured) {
+      hipError_t e = hipFuncSetAttribute((const void*)gemm_small_m_lds_kernel<T>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+      if (e != hipSuccess) return e;
+      configured = true;
+    }
+    hipLaunchKernelGGL((gemm_small_m_lds_kernel<T>), dim3((unsigned)grid), dim3(64 * kSmWaves),
+                       kLds, stream, qx, sx, qw, sw, bias, M, N, K, y);
+    return hipGetLastError();
+  }
+  constexpr int G = T <= 4 ? 8 : 4;
   hipLaunchKernelGGL((gemm_small_m_kernel<T, G>), dim3((unsigned)grid), dim3(64 * kSmWaves), 0,
                      stream, qx, sx, qw, sw, bias, M, N, K, y);
   return hipGetLastError();
