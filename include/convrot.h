@@ -27,6 +27,10 @@
  *     host, allocates memory, or keeps a pointer after it returns.  Calls on
  *     different streams that share output buffers race.
  *   - Outputs must not alias inputs.
+ *   - The batch size may be 0 (M rows of activations or gradients, the rows of a
+ *     weight, T ids): the call then checks its other sizes, enqueues nothing and
+ *     returns CONVROT_OK without reading any pointer (they may be NULL).  Every
+ *     other size must be positive.
  *   - Arguments are validated on the host before anything is enqueued; on any
  *     error nothing is launched and a negative status is returned.  Faults inside
  *     kernels surface asynchronously on the stream, as for any HIP launch.
@@ -45,7 +49,7 @@ extern "C" {
 
 /* Status codes. */
 #define CONVROT_OK 0
-#define CONVROT_EINVAL (-1)     /* null pointer, non-positive size, misaligned pointer */
+#define CONVROT_EINVAL (-1)     /* null pointer, negative or zero size, misaligned pointer */
 #define CONVROT_ESHAPE (-2)     /* block != 128, K or D not a multiple of 128, size over a limit */
 #define CONVROT_EWORKSPACE (-3) /* workspace too small */
 #define CONVROT_EHIP (-4)       /* a HIP call or launch failed */
@@ -147,7 +151,8 @@ int convrot_embedding_lookup(const int32_t* ids, int64_t T, const int8_t* qe, co
                              int64_t V, int64_t D, uint16_t* out, int32_t* oob_count,
                              hipStream_t stream);
 
-/* Workspace bytes needed by an operation (0 on invalid sizes). */
+/* Workspace bytes needed by an operation (0 on invalid sizes, and for an empty
+ * batch, which needs none). */
 size_t convrot_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t mode);
 
 /* Human-readable text of a status code (static storage). */

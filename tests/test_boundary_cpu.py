@@ -81,7 +81,8 @@ def test_null_pointers_are_einval(cr):
 
 def test_bad_sizes_and_shapes(cr):
     L = cr.lib()
-    assert L.convrot_linear_fwd(A, 0, 128, B, B, 4, None, Y, WS, 1 << 20, None) == -1
+    assert L.convrot_linear_fwd(A, -1, 128, B, B, 4, None, Y, WS, 1 << 20, None) == -1
+    assert L.convrot_linear_fwd(A, 4, 128, B, B, 0, None, Y, WS, 1 << 20, None) == -1
     assert L.convrot_linear_fwd(A, 4, 100, B, B, 4, None, Y, WS, 1 << 20, None) == -2
     assert L.convrot_linear_fwd(A, 4, 128 * 257, B, B, 4, None, Y, WS, 1 << 30, None) == -2
     assert L.convrot_quantize_weight(A, 4, 128, 64, 0, B, Y, None) == -2
@@ -96,6 +97,37 @@ def test_bad_sizes_and_shapes(cr):
                                      None) == -2
     assert L.convrot_linear_fwd_lora(A, 4, 128, B, B, 4, None, A, B, 16, 1.0, Y, WS, 512,
                                      None) == -3
+
+
+def test_empty_batch_is_a_no_op(cr):
+    """A batch of 0 rows / tokens / ids enqueues nothing and touches no pointer
+    (all NULL here, no stream, no GPU); the other sizes are still checked."""
+    L = cr.lib()
+    assert L.convrot_quantize_weight(None, 0, 256, 128, 0, None, None, None) == 0
+    assert L.convrot_quantize_weight(None, 0, 256, 64, 0, None, None, None) == -2
+    assert L.convrot_quantize_act(None, 0, 4096, None, None, None) == 0
+    assert L.convrot_quantize_act(None, 0, 100, None, None, None) == -2
+    assert L.convrot_bwd_quant_dy(None, 0, 4096, None, None, None, None) == 0
+    assert L.convrot_linear_fwd(None, 0, 4096, None, None, 4096, None, None, None, 0, None) == 0
+    assert L.convrot_linear_fwd(None, 0, 4000, None, None, 4096, None, None, None, 0, None) == -2
+    assert L.convrot_linear_fwd(None, 0, 4096, None, None, 0, None, None, None, 0, None) == -1
+    assert L.convrot_linear_fwd_lora(None, 0, 4096, None, None, 4096, None, None, None, 16, 1.0,
+                                     None, None, 0, None) == 0
+    assert L.convrot_linear_fwd_lora(None, 0, 4096, None, None, 4096, None, None, None, 8, 1.0,
+                                     None, None, 0, None) == -2
+    assert L.convrot_lora_down(None, 0, 4096, None, 32, None, None) == 0
+    assert L.convrot_gemm_i8_bf16(None, None, None, None, 0, 256, 256, None, None, None) == 0
+    assert L.convrot_gemm_i8_i32(None, None, 0, 256, 256, 1, None, None) == 0
+    assert L.convrot_gemm_i8_i32(None, None, 0, 100, 256, 1, None, None) == -2
+    for mode in (0, 1):
+        assert L.convrot_linear_bwd_dx(None, 0, 4096, None, None, 4096, mode, None, None, 0,
+                                       None) == 0
+    assert L.convrot_linear_bwd_dx(None, 0, 4096, None, None, 4096, 2, None, None, 0, None) == -1
+    assert L.convrot_embedding_lookup(None, 0, None, None, 10, 128, None, None, None) == 0
+    assert L.convrot_embedding_lookup(None, 0, None, None, 10, 96, None, None, None) == -2
+    for op, mode in ((cr.OP_LINEAR_FWD, 0), (cr.OP_LINEAR_FWD_LORA, 16),
+                     (cr.OP_LINEAR_BWD_DX, cr.BWD_INT8)):
+        assert cr.workspace_bytes(op, 0, 4096, 4096, mode) == 0
 
 
 def test_misalignment_is_einval(cr):

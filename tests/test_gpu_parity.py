@@ -322,3 +322,38 @@ def test_binding_rejects_mismatched_buffers(cr):
     acc = bad[-1]()
     torch.cuda.synchronize()
     assert tuple(acc.shape) == (128, 64) and int(acc.abs().max().item()) == 0
+
+
+def test_empty_batch(cr):
+    """A batch of 0 tokens / rows / ids goes through every entry point as a no-op
+    and returns empty outputs of the right shape; the lookup leaves its
+    out-of-range counter alone."""
+    say("empty batch through every entry point")
+    d = "cuda"
+    K, N = 4096, 512
+    w = bf16_to_dev(wl.packed_weight(77, 0, N, K))
+    qw, sw = cr.quantize_weight(w)
+    x0 = torch.empty((0, K), dtype=torch.bfloat16, device=d)
+    dy0 = torch.empty((0, N), dtype=torch.bfloat16, device=d)
+    a = torch.zeros((16, K), dtype=torch.bfloat16, device=d)
+    b = torch.zeros((N, 16), dtype=torch.bfloat16, device=d)
+    q0, s0 = cr.quantize_weight(x0)
+    assert tuple(q0.shape) == (0, K) and tuple(s0.shape) == (0,)
+    qa, sa = cr.quantize_act(x0)
+    assert tuple(qa.shape) == (0, K) and tuple(sa.shape) == (0,)
+    assert tuple(cr.linear_fwd(x0, qw, sw).shape) == (0, N)
+    assert tuple(cr.linear_fwd_lora(x0, qw, sw, a, b, 0.5).shape) == (0, N)
+    assert tuple(cr.lora_down(x0, a).shape) == (0, 16)
+    assert tuple(cr.gemm_i8_bf16(qa, sa, qw, sw).shape) == (0, N)
+    assert tuple(cr.gemm_i8_i32(qa, qw).shape) == (0, N)
+    qg, sg = cr.bwd_quant_dy(dy0, sw)
+    assert tuple(qg.shape) == (0, N) and tuple(sg.shape) == (0,)
+    for mode in (cr.BWD_BF16, cr.BWD_INT8):
+        assert tuple(cr.linear_bwd_dx(dy0, qw, sw, mode).shape) == (0, K)
+    oob = torch.full((1,), 7, dtype=torch.int32, device=d)
+    out = cr.embedding_lookup(torch.empty((0,), dtype=torch.int32, device=d), qw, sw, oob)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, K) and int(oob.item()) == 7
+    # the layer still works after the empty calls
+    x = bf16_to_dev(wl.activations(3, K, wl.n_outliers(K), base=1))
+    assert torch.equal(cr.linear_fwd(x, qw, sw), cr.gemm_i8_bf16(*cr.quantize_act(x), qw, sw))

@@ -35,9 +35,14 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONV
 
 bool row_len_ok(int64_t K) { return K > 0 && K % kBlock == 0 && K <= CONVROT_MAX_ROW_LEN; }
 
+// An empty batch (no rows, tokens or ids) enqueues nothing: only the other
+// sizes are checked, and the pointers are not looked at.
+inline int empty_batch(bool shape_ok) { return shape_ok ? CONVROT_OK : CONVROT_ESHAPE; }
+
 int quantize_rows_checked(const uint16_t* x, int64_t rows, int64_t K, int8_t* q, float* s,
                           int64_t chunk_rows, const float* colscale, bool fold,
                           hipStream_t stream) {
+  if (rows == 0 && K > 0 && chunk_rows >= 0) return empty_batch(row_len_ok(K));
   if (!x || !q || !s || rows <= 0 || K <= 0 || chunk_rows < 0) return CONVROT_EINVAL;
   if (fold && !colscale) return CONVROT_EINVAL;
   if (!aligned16(x) || !aligned16(q) || (colscale && !aligned16(colscale))) return CONVROT_EINVAL;
@@ -99,7 +104,7 @@ size_t convrot_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int3
 
 int convrot_quantize_weight(const uint16_t* w, int64_t rows, int64_t cols, int32_t block,
                             int64_t chunk_rows, int8_t* q, float* scale, hipStream_t stream) {
-  if (block != kBlock) return w && q && scale ? CONVROT_ESHAPE : CONVROT_EINVAL;
+  if (block != kBlock) return (rows == 0 || (w && q && scale)) ? CONVROT_ESHAPE : CONVROT_EINVAL;
   return quantize_rows_checked(w, rows, cols, q, scale, chunk_rows, nullptr, false, stream);
 }
 
@@ -116,6 +121,7 @@ int convrot_bwd_quant_dy(const uint16_t* dy, int64_t M, int64_t N, const float* 
 int convrot_gemm_i8_bf16(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw,
                          int64_t M, int64_t N, int64_t K, const uint16_t* bias, uint16_t* y,
                          hipStream_t stream) {
+  if (M == 0 && N > 0 && K > 0) return empty_batch(K % kBlock == 0);
   if (!qx || !sx || !qw || !sw || !y || M <= 0 || N <= 0 || K <= 0) return CONVROT_EINVAL;
   if (!aligned16(qx) || !aligned16(qw) || !aligned16(y)) return CONVROT_EINVAL;
   if (K % kBlock) return CONVROT_ESHAPE;
@@ -130,6 +136,7 @@ int convrot_gemm_i8_bf16(const int8_t* qx, const float* sx, const int8_t* qw, co
 int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw,
                        const float* sw, int64_t N, const uint16_t* bias, uint16_t* y,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (M == 0 && N > 0 && K > 0) return empty_batch(row_len_ok(K));
   if (!x || !qw || !sw || !y || !workspace || M <= 0 || N <= 0 || K <= 0) return CONVROT_EINVAL;
   if (!aligned16(x) || !aligned16(qw) || !aligned16(y) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255))
@@ -161,6 +168,7 @@ int convrot_linear_fwd_lora(const uint16_t* x, int64_t M, int64_t K, const int8_
                             const uint16_t* lora_a, const uint16_t* lora_b, int32_t R,
                             float lora_scale, uint16_t* y, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
+  if (M == 0 && N > 0 && K > 0) return empty_batch(row_len_ok(K) && (R == 16 || R == 32));
   if (!x || !qw || !sw || !y || !lora_a || !lora_b || !workspace || M <= 0 || N <= 0 || K <= 0)
     return CONVROT_EINVAL;
   if (!aligned16(x) || !aligned16(qw) || !aligned16(y) || !aligned16(lora_a) ||
@@ -187,6 +195,7 @@ int convrot_linear_fwd_lora(const uint16_t* x, int64_t M, int64_t K, const int8_
 
 int convrot_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint16_t* lora_a,
                       int32_t R, uint16_t* xa, hipStream_t stream) {
+  if (M == 0 && K > 0) return empty_batch(row_len_ok(K) && (R == 16 || R == 32));
   if (!x || !lora_a || !xa || M <= 0 || K <= 0) return CONVROT_EINVAL;
   if (!aligned16(x) || !aligned16(lora_a)) return CONVROT_EINVAL;
   if (!row_len_ok(K) || (R != 16 && R != 32)) return CONVROT_ESHAPE;
@@ -197,6 +206,8 @@ int convrot_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint16_t* l
 
 int convrot_gemm_i8_i32(const int8_t* a_, const int8_t* b, int64_t M, int64_t N, int64_t K,
                         int32_t b_layout, int32_t* acc, hipStream_t stream) {
+  if (M == 0 && N > 0 && K > 0 && (b_layout == 0 || b_layout == 1))
+    return empty_batch(K % kBlock == 0 && (b_layout == 0 || N % kBlock == 0));
   if (!a_ || !b || !acc || M <= 0 || N <= 0 || K <= 0) return CONVROT_EINVAL;
   if (!aligned16(a_) || !aligned16(b) || !aligned16(acc)) return CONVROT_EINVAL;
   if (b_layout != 0 && b_layout != 1) return CONVROT_EINVAL;
@@ -223,6 +234,9 @@ int convrot_dequant_weight_t(const int8_t* qw, const float* sw, int64_t N, int64
 int convrot_linear_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, const int8_t* qw,
                           const float* sw, int64_t K, int32_t mode, uint16_t* dx,
                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (M == 0 && N > 0 && K > 0 && (mode == CONVROT_BWD_BF16 || mode == CONVROT_BWD_INT8))
+    return empty_batch(K % kBlock == 0 && N % kBlock == 0 &&
+                       (mode != CONVROT_BWD_INT8 || N <= CONVROT_MAX_ROW_LEN));
   if (!dy || !qw || !sw || !dx || !workspace || M <= 0 || N <= 0 || K <= 0) return CONVROT_EINVAL;
   if (mode != CONVROT_BWD_BF16 && mode != CONVROT_BWD_INT8) return CONVROT_EINVAL;
   if (!aligned16(dy) || !aligned16(qw) || !aligned16(sw) || !aligned16(dx) ||
@@ -256,6 +270,7 @@ int convrot_linear_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, const int8_t
 int convrot_embedding_lookup(const int32_t* ids, int64_t T, const int8_t* qe, const float* se,
                              int64_t V, int64_t D, uint16_t* out, int32_t* oob_count,
                              hipStream_t stream) {
+  if (T == 0 && V > 0 && D > 0) return empty_batch(D % kBlock == 0);
   if (!ids || !qe || !se || !out || T <= 0 || V <= 0 || D <= 0) return CONVROT_EINVAL;
   if (!aligned16(qe) || !aligned16(out)) return CONVROT_EINVAL;
   if (D % kBlock) return CONVROT_ESHAPE;

@@ -312,8 +312,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
   // 256 s_i values are copied to LDS together with the first stage.
   constexpr bool kScales =
       EPI == kEpiDequantBf16 || EPI == kEpiDequantLoraBf16 || EPI == kEpiInvRotBf16;
+  // The LoRA epilogue of rank 16 leaves 16 KB of its 32 KB LDS region free,
+  // enough for the s_i values too; rank 32 reads them from global memory.
   constexpr bool kTileScales = EPI == kEpiDequantBf16 && !PT;
-  const float* const si_tile = reinterpret_cast<const float*>(lds + STAGES * 2 * kTile * BK);
+  const bool tile_scales = kTileScales || (EPI == kEpiDequantLoraBf16 && a.lora_r == 16);
+  const float* const si_tile = reinterpret_cast<const float*>(
+      lds + STAGES * 2 * kTile * BK + (EPI == kEpiDequantLoraBf16 ? 2 * kTile * 32 : 0));
   float sj_pre[NJ];
 #pragma unroll
   for (int y = 0; y < NJ; ++y) {
@@ -521,7 +525,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
       for (int t = 0; t < NJ; ++t)
         f[NI + t] = *reinterpret_cast<const uint4*>(qs + lds_off<BK>(wj * TJ + t * 32 + (lane & 31), chunk));
     };
-    if constexpr (kTileScales) {
+    if (tile_scales) {
       // older than the stage loads, so complete once stage 0 is, and published
       // by the same barrier
       if (wave < kTile / 64) {
@@ -644,9 +648,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
       *reinterpret_cast<uint2*>(stg + jl * kRowBytes + pos * 16 + (il & 7) * 2) = make_uint2(lo, hi);
     };
     // Write the staged rows 32 y0 .. 32 (y0 + ny) - 1 of this wave's sub-tile:
-    // 16-byte chunks of contiguous output rows, 64 lanes per step.  The plain
-    // dequantizing epilogue calls it after each y, so the stores of one slice
-    // are in flight while the next is converted.
+    // 16-byte chunks of contiguous output rows, 64 lanes per step.  The
+    // dequantizing epilogues (with or without LoRA) call it after each y, so the
+    // stores of one slice are in flight while the next is converted.
     uint16_t* out = static_cast<uint16_t*>(a.out);
     auto flush = [&](int y0, int ny) {
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes landed
@@ -746,8 +750,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
             float v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) v[u] = (float)acc[x][y][4 * g + u];
-            if constexpr (kTileScales) dequant4_tile(v, sjv, si_tile, a.bias, i, i0, a.I);
-            else if constexpr (kDequant) dequant4(v, sjv, a.si, a.bias, i, a.I);
+            if constexpr (kTileScales) {
+              dequant4_tile(v, sjv, si_tile, a.bias, i, i0, a.I);
+            } else if constexpr (kLora) {
+              if (tile_scales) dequant4_tile(v, sjv, si_tile, a.bias, i, i0, a.I);
+              else dequant4(v, sjv, a.si, a.bias, i, a.I);
+            } else if constexpr (kDequant) {
+              dequant4(v, sjv, a.si, a.bias, i, a.I);
+            }
             if constexpr (kLora) {
 #pragma unroll
               for (int u = 0; u < 4; ++u) v[u] = v[u] + a.lora_scale * lo[4 * g + u];
@@ -755,9 +765,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
             put8(jl, il, pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
           }
         }
-        if constexpr (!kLora) flush(y, 1);
+        flush(y, 1);
       }
-      if constexpr (kLora) flush(0, NJ);
     }
   }
 }
