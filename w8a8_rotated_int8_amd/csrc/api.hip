@@ -40,7 +40,7 @@ bool row_len_ok(int64_t K) { return K > 0 && K % kBlock == 0 && K <= CONVROT_MAX
 inline int empty_batch(bool shape_ok) { return shape_ok ? CONVROT_OK : CONVROT_ESHAPE; }
 
 int quantize_rows_checked(const uint16_t* x, int64_t rows, int64_t K, int8_t* q, float* s,
-                          int64_t chunk_rows, const float* colscale, bool fold,
+                          int64_t chunk_rows, const float* colscale, bool fold, bool weights,
                           hipStream_t stream) {
   if (rows == 0 && K > 0 && chunk_rows >= 0) return empty_batch(row_len_ok(K));
   if (!x || !q || !s || rows <= 0 || K <= 0 || chunk_rows < 0) return CONVROT_EINVAL;
@@ -53,7 +53,7 @@ int quantize_rows_checked(const uint16_t* x, int64_t rows, int64_t K, int8_t* q,
   for (int64_t r0 = 0; r0 < rows; r0 += chunk_rows) {
     int64_t n = rows - r0 < chunk_rows ? rows - r0 : chunk_rows;
     hipError_t e = launch_rotate_quant(x + r0 * K, n, (int)K, q + r0 * K, s + r0, colscale, fold,
-                                       stream);
+                                       weights, stream);
     if (e != hipSuccess) return CONVROT_EHIP;
   }
   return CONVROT_OK;
@@ -105,17 +105,17 @@ size_t convrot_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int3
 int convrot_quantize_weight(const uint16_t* w, int64_t rows, int64_t cols, int32_t block,
                             int64_t chunk_rows, int8_t* q, float* scale, hipStream_t stream) {
   if (block != kBlock) return (rows == 0 || (w && q && scale)) ? CONVROT_ESHAPE : CONVROT_EINVAL;
-  return quantize_rows_checked(w, rows, cols, q, scale, chunk_rows, nullptr, false, stream);
+  return quantize_rows_checked(w, rows, cols, q, scale, chunk_rows, nullptr, false, true, stream);
 }
 
 int convrot_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* qx, float* sx,
                          hipStream_t stream) {
-  return quantize_rows_checked(x, M, K, qx, sx, 0, nullptr, false, stream);
+  return quantize_rows_checked(x, M, K, qx, sx, 0, nullptr, false, false, stream);
 }
 
 int convrot_bwd_quant_dy(const uint16_t* dy, int64_t M, int64_t N, const float* sw, int8_t* qg,
                          float* sg, hipStream_t stream) {
-  return quantize_rows_checked(dy, M, N, qg, sg, 0, sw, true, stream);
+  return quantize_rows_checked(dy, M, N, qg, sg, 0, sw, true, false, stream);
 }
 
 int convrot_gemm_i8_bf16(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw,
@@ -148,7 +148,7 @@ int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw
   if (st) return st;
   int8_t* qx = static_cast<int8_t*>(workspace);
   float* sx = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + align256((size_t)M * K));
-  hipError_t e = launch_rotate_quant(x, M, (int)K, qx, sx, nullptr, false, stream);
+  hipError_t e = launch_rotate_quant(x, M, (int)K, qx, sx, nullptr, false, false, stream);
   if (e != hipSuccess) return CONVROT_EHIP;
   if (use_small_m(M, N, K))
     return hip_status(launch_gemm_small_m(qx, sx, qw, sw, bias, M, N, K, y, stream));
@@ -183,7 +183,7 @@ int convrot_linear_fwd_lora(const uint16_t* x, int64_t M, int64_t K, const int8_
   int8_t* qx = reinterpret_cast<int8_t*>(ws);
   float* sx = reinterpret_cast<float*>(ws + align256((size_t)M * K));
   uint16_t* xa = reinterpret_cast<uint16_t*>(ws + xa_off);
-  hipError_t e = launch_rotate_quant(x, M, (int)K, qx, sx, nullptr, false, stream);
+  hipError_t e = launch_rotate_quant(x, M, (int)K, qx, sx, nullptr, false, false, stream);
   if (e == hipSuccess) e = launch_lora_down(x, M, K, lora_a, R, xa, stream);
   if (e != hipSuccess) return CONVROT_EHIP;
   GemmArgs a{};
@@ -251,7 +251,7 @@ int convrot_linear_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, const int8_t
   if (mode == CONVROT_BWD_INT8) {
     int8_t* qg = static_cast<int8_t*>(workspace);
     float* sg = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + align256((size_t)M * N));
-    hipError_t e = launch_rotate_quant(dy, M, (int)N, qg, sg, sw, true, stream);
+    hipError_t e = launch_rotate_quant(dy, M, (int)N, qg, sg, sw, true, false, stream);
     if (e != hipSuccess) return CONVROT_EHIP;
     GemmArgs a{};
     a.P = qw; a.Q = qg; a.I = K; a.J = M; a.Kc = N; a.ldp = K; a.ldq = N;

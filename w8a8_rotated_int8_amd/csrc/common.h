@@ -164,6 +164,23 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// dma16 with the non-temporal cache policy, for data read exactly once (the
+// rows of a weight or embedding being quantized).
+__device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// 16-byte store with the non-temporal cache policy, for outputs that this
+// library does not read back (measured faster than plain stores on gfx950 for
+// long write streams).
+__device__ __forceinline__ void store16_nt(void* dst, uint4 v) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(dst));
+}
+
 // 4-byte direct global->LDS load (lane i's word lands at lds_base + 4 i); the
 // same ordering rules as dma16.
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {

@@ -650,7 +650,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
     // Write the staged rows 32 y0 .. 32 (y0 + ny) - 1 of this wave's sub-tile:
     // 16-byte chunks of contiguous output rows, 64 lanes per step.  The
     // dequantizing epilogues (with or without LoRA) call it after each y, so the
-    // stores of one slice are in flight while the next is converted.
+    // stores of one slice are in flight while the next is converted.  The stores
+    // are non-temporal: nothing here reads the output back, and the 4096^3
+    // forward measured ~1.3 us faster than with plain stores.
     uint16_t* out = static_cast<uint16_t*>(a.out);
     auto flush = [&](int y0, int ny) {
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes landed
@@ -667,7 +669,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
         if (j >= a.J || i >= a.I) continue;
         uint16_t* dst = out + j * a.ldo + i;
         if (i + 8 <= a.I) {
-          *reinterpret_cast<uint4*>(dst) = v;
+          store16_nt(dst, v);
         } else {
           const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
           for (int u = 0; u < 8 && i + u < a.I; ++u) dst[u] = (uint16_t)(wds[u >> 1] >> (16 * (u & 1)));

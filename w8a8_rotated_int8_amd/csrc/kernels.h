@@ -18,8 +18,12 @@ RowPlan plan_rows(int K);
 
 // Rotate (fold == false) or scale-fold (fold == true, colscale[K]) each row of
 // x [rows, K] and quantize it per row to int8 codes q and fp32 scales.
+// weights: x is read once and q is not read back soon (load-time quantization),
+// so both move with the non-temporal cache policy; activations and gradients
+// are read again (LoRA branch) or their codes are (the GEMM that follows).
 hipError_t launch_rotate_quant(const uint16_t* x, int64_t rows, int K, int8_t* q, float* scale,
-                               const float* colscale, bool fold, hipStream_t stream);
+                               const float* colscale, bool fold, bool weights,
+                               hipStream_t stream);
 
 // Epilogues of the tiled GEMM out[j][i] = sum_k P[i][k] * Q[j][k].
 enum GemmEpilogue {

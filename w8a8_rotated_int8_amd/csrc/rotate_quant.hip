@@ -26,8 +26,9 @@ constexpr int kSpan = CONVROT_SPAN;
 
 // Short rows (K < 128 * kSpan): one task of rows_per_wave packed rows per wave,
 // in its own LDS buffer; the resident waves of a SIMD cover each other's load
-// latency.
-template <int MODE, int SB>
+// latency.  STREAM (weights): loads and code stores bypass-cache (read once,
+// not read back soon).
+template <int MODE, int SB, bool STREAM>
 __global__ __launch_bounds__(256) void rotate_quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int K, int8_t* __restrict__ q,
     float* __restrict__ scale, const float* __restrict__ colscale, int rows_per_wave) {
@@ -42,18 +43,18 @@ __global__ __launch_bounds__(256) void rotate_quant_rows_kernel(
   const int64_t r0 = task * rows_per_wave;
   const int64_t rh = rows - r0;
   const int nbk = (rh < rows_per_wave ? (int)rh : rows_per_wave) * nb;
-  stage_span<SB>(x, r0 * (int64_t)K, nbk, buf);
+  stage_span<SB, STREAM>(x, r0 * (int64_t)K, nbk, buf);
   uint8_t* cs = lds + 4 * span_bytes<SB>() + wave * SB * 512;  // fold mode: column scales
   if constexpr (MODE == kFold) stage_colscale<SB>(colscale, nbk, nb, 0, 1, cs);
   wait_vm_n<0>();
-  quantize_span<MODE, SB, MODE == kFold>(buf, nbk, nb, r0 * (int64_t)K, 0, r0, 1, q, scale,
-                                         colscale, seg_max[wave], nullptr, cs);
+  quantize_span<MODE, SB, MODE == kFold, STREAM>(buf, nbk, nb, r0 * (int64_t)K, 0, r0, 1, q,
+                                                 scale, colscale, seg_max[wave], nullptr, cs);
 }
 
 // Long rows (K >= 128 * kSpan): one row per workgroup, one SB-block slice per
 // wave; the waves combine their maxima through LDS.  CSL (fold mode): the
 // column scales of each slice are staged in LDS past the rows' slices.
-template <int MODE, int SB, bool CSL>
+template <int MODE, int SB, bool CSL, bool STREAM>
 __global__ __launch_bounds__(SB == 16 ? 1024 : 512) void rotate_quant_long_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int K, int8_t* __restrict__ q,
     float* __restrict__ scale, const float* __restrict__ colscale, int waves_per_row) {
@@ -67,13 +68,14 @@ __global__ __launch_bounds__(SB == 16 ? 1024 : 512) void rotate_quant_long_kerne
   const int span_blocks = rem < SB ? rem : SB;
   const int64_t span_elem0 = row0 * (int64_t)K + (int64_t)blk_in_row0 * kBlock;
   uint8_t* my_lds = lds + wave * span_bytes<SB>();
-  stage_span<SB>(x, span_elem0, span_blocks, my_lds);
+  stage_span<SB, STREAM>(x, span_elem0, span_blocks, my_lds);
   uint8_t* cs = lds + waves_per_row * span_bytes<SB>() + wave * SB * 512;
   if constexpr (CSL)
     stage_colscale<SB>(colscale, span_blocks, nb, blk_in_row0, waves_per_row, cs);
   wait_vm_n<0>();
-  quantize_span<MODE, SB, CSL>(my_lds, span_blocks, nb, span_elem0, blk_in_row0, row0,
-                               waves_per_row, q, scale, colscale, nullptr, row_part_max, cs);
+  quantize_span<MODE, SB, CSL, STREAM>(my_lds, span_blocks, nb, span_elem0, blk_in_row0, row0,
+                                       waves_per_row, q, scale, colscale, nullptr, row_part_max,
+                                       cs);
 }
 
 }  // namespace
@@ -96,8 +98,9 @@ RowPlan plan_rows(int K) {
 }
 
 hipError_t launch_rotate_quant(const uint16_t* x, int64_t rows, int K, int8_t* q, float* scale,
-                               const float* colscale, bool fold, hipStream_t stream) {
+                               const float* colscale, bool fold, bool weights, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
+  if (fold && weights) return hipErrorInvalidValue;
   RowPlan pl = plan_rows(K);
   // Fold-mode column scales staged in LDS cost 8 KB per wave beside its 4 KB
   // span.  They are staged when a CU still holds at least 12 waves of the
@@ -109,11 +112,13 @@ hipError_t launch_rotate_quant(const uint16_t* x, int64_t rows, int K, int8_t* q
   if (!configured) {
     hipError_t e = hipSuccess;
     const int max_lds = CONVROT_MAX_ROW_LEN_BLOCKS * 256;
-    const void* ks[3] = {(const void*)rotate_quant_long_kernel<kRotate, kSpan, false>,
-                         (const void*)rotate_quant_long_kernel<kFold, kSpan, false>,
-                         (const void*)rotate_quant_long_kernel<kFold, kSpan, true>};
-    const int lim[3] = {max_lds, max_lds, kMaxCslWaves * (span_bytes<kSpan>() + kSpan * 512)};
-    for (int k = 0; k < 3; ++k) {
+    const void* ks[4] = {(const void*)rotate_quant_long_kernel<kRotate, kSpan, false, false>,
+                         (const void*)rotate_quant_long_kernel<kRotate, kSpan, false, true>,
+                         (const void*)rotate_quant_long_kernel<kFold, kSpan, false, false>,
+                         (const void*)rotate_quant_long_kernel<kFold, kSpan, true, false>};
+    const int lim[4] = {max_lds, max_lds, max_lds,
+                        kMaxCslWaves * (span_bytes<kSpan>() + kSpan * 512)};
+    for (int k = 0; k < 4; ++k) {
       e = hipFuncSetAttribute(ks[k], hipFuncAttributeMaxDynamicSharedMemorySize, lim[k]);
       if (e != hipSuccess) return e;
     }
@@ -124,12 +129,16 @@ hipError_t launch_rotate_quant(const uint16_t* x, int64_t rows, int K, int8_t* q
     const int64_t grid = (tasks + 3) / 4;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     if (fold)
-      hipLaunchKernelGGL((rotate_quant_rows_kernel<kFold, kSpan>), dim3((unsigned)grid), dim3(256),
-                         4 * (span_bytes<kSpan>() + kSpan * 512), stream, x, rows, K, q, scale,
-                         colscale, pl.rows_per_wave);
+      hipLaunchKernelGGL((rotate_quant_rows_kernel<kFold, kSpan, false>), dim3((unsigned)grid),
+                         dim3(256), 4 * (span_bytes<kSpan>() + kSpan * 512), stream, x, rows, K, q,
+                         scale, colscale, pl.rows_per_wave);
+    else if (weights)
+      hipLaunchKernelGGL((rotate_quant_rows_kernel<kRotate, kSpan, true>), dim3((unsigned)grid),
+                         dim3(256), 4 * span_bytes<kSpan>(), stream, x, rows, K, q, scale, colscale,
+                         pl.rows_per_wave);
     else
-      hipLaunchKernelGGL((rotate_quant_rows_kernel<kRotate, kSpan>), dim3((unsigned)grid), dim3(256),
-                         4 * span_bytes<kSpan>(), stream, x, rows, K, q, scale, colscale,
+      hipLaunchKernelGGL((rotate_quant_rows_kernel<kRotate, kSpan, false>), dim3((unsigned)grid),
+                         dim3(256), 4 * span_bytes<kSpan>(), stream, x, rows, K, q, scale, colscale,
                          pl.rows_per_wave);
   } else {
     if (rows > 0x7fffffff) return hipErrorInvalidValue;
@@ -138,17 +147,21 @@ hipError_t launch_rotate_quant(const uint16_t* x, int64_t rows, int K, int8_t* q
     const bool csl = pl.waves_per_row <= kMaxCslWaves &&
                      (kLdsPerCu / csl_wg) * pl.waves_per_row >= 12;
     if (fold && csl)
-      hipLaunchKernelGGL((rotate_quant_long_kernel<kFold, kSpan, true>), dim3((unsigned)rows),
+      hipLaunchKernelGGL((rotate_quant_long_kernel<kFold, kSpan, true, false>), dim3((unsigned)rows),
                          dim3(pl.threads), lds + (size_t)pl.waves_per_row * kSpan * 512, stream, x,
                          rows, K, q, scale, colscale, pl.waves_per_row);
     else if (fold)
-      hipLaunchKernelGGL((rotate_quant_long_kernel<kFold, kSpan, false>), dim3((unsigned)rows),
+      hipLaunchKernelGGL((rotate_quant_long_kernel<kFold, kSpan, false, false>), dim3((unsigned)rows),
+                         dim3(pl.threads), lds, stream, x, rows, K, q, scale, colscale,
+                         pl.waves_per_row);
+    else if (weights)
+      hipLaunchKernelGGL((rotate_quant_long_kernel<kRotate, kSpan, false, true>), dim3((unsigned)rows),
                          dim3(pl.threads), lds, stream, x, rows, K, q, scale, colscale,
                          pl.waves_per_row);
     else
-      hipLaunchKernelGGL((rotate_quant_long_kernel<kRotate, kSpan, false>), dim3((unsigned)rows),
-                         dim3(pl.threads), lds, stream, x, rows, K, q, scale, colscale,
-                         pl.waves_per_row);
+      hipLaunchKernelGGL((rotate_quant_long_kernel<kRotate, kSpan, false, false>),
+                         dim3((unsigned)rows), dim3(pl.threads), lds, stream, x, rows, K, q, scale,
+                         colscale, pl.waves_per_row);
   }
   return hipGetLastError();
 }

@@ -63,7 +63,7 @@ __device__ __forceinline__ void swap_rows16(double& vdst, double& src0) {
 // register bit 4 with a lane bit, so that the butterfly partners meet in one
 // lane.  After both, lane quarter q = L >> 4 holds outputs 16 q + e in v[e]
 // and 64 + 16 q + e in v[e + 16] (e < 16).
-template <int MODE, int SB = kSpanBlocks, bool CSL = false>
+template <int MODE, int SB = kSpanBlocks, bool CSL = false, bool STREAM = false>
 __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_blocks, int nb,
                                               int64_t span_elem0, int blk_in_row0, int64_t row0,
                                               int waves_per_row, int8_t* __restrict__ q,
@@ -271,15 +271,22 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
 #pragma unroll
   for (int j = 0; j < SB / 8; ++j) {
     const int c = 64 * j + lane;
-    if (c < nchunks)
-      *reinterpret_cast<uint4*>(dst + 16 * c) = *reinterpret_cast<const uint4*>(stg + 16 * phys(c));
+    if (c < nchunks) {
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + 16 * phys(c));
+      // codes of a weight are not read again soon; activation and gradient
+      // codes are, by the GEMM that follows
+      if constexpr (STREAM) store16_nt(dst + 16 * c, v);
+      else *reinterpret_cast<uint4*>(dst + 16 * c) = v;
+    }
   }
 }
 
 // Issue the SB/4 direct-to-LDS loads of a span of span_blocks (1..SB) blocks.
 // Slots past the span reload its last chunk so every lane always issues the
 // same number of loads (the vmcnt bookkeeping relies on it).
-template <int SB = kSpanBlocks>
+// STREAM: the rows are read once (load-time weight quantization): loads with
+// the non-temporal cache policy.
+template <int SB = kSpanBlocks, bool STREAM = false>
 __device__ __forceinline__ void stage_span(const uint16_t* __restrict__ x, int64_t span_elem0,
                                            int span_blocks, uint8_t* my_lds) {
   const int lane = threadIdx.x & 63;
@@ -290,7 +297,8 @@ __device__ __forceinline__ void stage_span(const uint16_t* __restrict__ x, int64
     int b = slot >> 4;
     int c = (slot & 15) ^ (b & 7);
     if (b >= span_blocks) { b = span_blocks - 1; c = 15; }
-    dma16(x + span_elem0 + (int64_t)b * kBlock + c * 8, base + i * 1024);
+    if constexpr (STREAM) dma16_nt(x + span_elem0 + (int64_t)b * kBlock + c * 8, base + i * 1024);
+    else dma16(x + span_elem0 + (int64_t)b * kBlock + c * 8, base + i * 1024);
   }
 }
 
