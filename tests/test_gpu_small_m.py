@@ -32,8 +32,12 @@ def cr():
     return cr
 
 
+# Row-tile counts 1..8 of the few-row kernel: ceil(M / 16) = 1 (1, 7, 16), 3 (33),
+# 4 (64), 5 (77), 6 (90), 7 (100, 110) and 8 (128); the q_x-in-LDS variant for
+# 3..8 tiles at K <= 4096 (three chunk buffers up to 6 tiles, two from 7 on).
 SHAPES = [(1, 4096, 4096), (7, 4096, 4096), (77, 4096, 4096), (128, 4096, 4096),
           (33, 4096, 3000), (16, 8192, 2048), (100, 8192, 4096), (300, 4096, 4096),
+          (64, 4096, 4096), (90, 4096, 2048), (110, 2048, 4096), (47, 1024, 2048),
           (77, 4096, 12288), (77, 12288, 4096), (77, 4096, 32), (4096, 4096, 32), (129, 512, 640)]
 
 

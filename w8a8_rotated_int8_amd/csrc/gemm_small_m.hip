@@ -95,28 +95,26 @@ __global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_kernel(
 
 // The same contraction with q_x staged through LDS.  K runs in chunks of 512
 // bytes; a chunk of all 16 T rows of q_x arrives by whole-line direct loads
-// (8 T instructions of 1 KB, T per wave) into one of two LDS buffers while the
-// previous chunk is multiplied, and wave w multiplies the chunk's 64-byte step
-// w.  Row r's 16-byte piece c sits at r * 512 + 16 (c ^ (r & 15)), so the 16
+// (8 T instructions of 1 KB, T per wave) into a ring of NB LDS buffers, NB - 1
+// chunks ahead of the one being multiplied, and wave w multiplies the chunk's
+// 64-byte step w.  Row r's 16-byte piece c sits at r * 512 + 16 (c ^ (r & 15)), so the 16
 // rows of one fragment read fall in different banks.  The waves' q_w steps of
-// every chunk (K <= 4096: at most 8 per wave) are loaded at the start with
-// loads the compiler does not track, so that its waits do not cover the
-// direct loads issued after them.
+// every chunk (K <= 4096: at most 8 per wave) are loaded at the start, before
+// the first chunk's direct loads, and the explicit wait for that chunk covers
+// them.  They are ordinary loads: the compiler must know when their registers
+// are written.  (Loads issued through inline asm were tried: the compiler then
+// took the registers as written at once and was free to copy them before the
+// data arrived, which it did in some instances.)
 constexpr int kSmChunk = 512;
 constexpr int kSmMaxChunks = 8;
 
-__device__ __forceinline__ uint4 load16_untracked(const void* p) {
-  uint4 v;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-
-template <int T>
+template <int T, int NB>
 __global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_lds_kernel(
     const int8_t* __restrict__ qx, const float* __restrict__ sx, const int8_t* __restrict__ qw,
     const float* __restrict__ sw, const uint16_t* __restrict__ bias, int64_t M, int64_t N,
     int64_t K, uint16_t* __restrict__ y) {
-  extern __shared__ __align__(16) uint8_t xs[];  // two buffers of 16 T rows x 512 bytes
+  static_assert(NB == 2 || NB == 3, "two or three chunk buffers");
+  extern __shared__ __align__(16) uint8_t xs[];  // NB buffers of 16 T rows x 512 bytes
   __shared__ int32_t part[T][4][64];
   for (int i = threadIdx.x; i < T * 256; i += 64 * kSmWaves) (&part[0][0][0])[i] = 0;
   const int lane = threadIdx.x & 63;
@@ -130,8 +128,9 @@ __global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_lds_kernel(
     const int8_t* wrow = qw + n * K + 64 * wave + 16 * g;
 #pragma unroll
     for (int c = 0; c < kSmMaxChunks; ++c)  // past the last chunk: reload it (unused)
-      wv[c] = load16_untracked(wrow + (c < nch ? c : nch - 1) * kSmChunk);
+      wv[c] = *reinterpret_cast<const uint4*>(wrow + (c < nch ? c : nch - 1) * kSmChunk);
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep the q_w loads ahead of the chunk loop
   constexpr int kBuf = 16 * T * kSmChunk;
   const uint32_t xs_base = __builtin_amdgcn_readfirstlane(lds_u32(xs));
   auto stage = [&](int c, int b) {
@@ -148,19 +147,22 @@ __global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_lds_kernel(
   v4i acc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = v4i{0, 0, 0, 0};
-  stage(0, 0);
+#pragma unroll
+  for (int c = 0; c < NB - 1; ++c)
+    if (c < nch) stage(c, c);
 #pragma unroll
   for (int c = 0; c < kSmMaxChunks; ++c) {
     if (c >= nch) break;
-    wait_vm_n<0>();  // this wave's part of chunk c landed (and, older, its q_w loads)
-    if (c == 0) {
-#pragma unroll
-      for (int cc = 0; cc < kSmMaxChunks; ++cc)  // q_w values are used after the wait
-        asm volatile("" : "+v"(wv[cc].x), "+v"(wv[cc].y), "+v"(wv[cc].z), "+v"(wv[cc].w));
-    }
+    // this wave's part of chunk c landed (and, older, its q_w loads); with
+    // three buffers chunk c + 1 may still be in flight.  The first wait is a
+    // full one: after it the compiler knows that every q_w load has landed and
+    // inserts no waits of its own later (those would count the direct loads
+    // issued since, which it does not see, and wait for them too).
+    if (c > 0 && NB == 3 && c + 1 < nch) wait_vm_n<T>();
+    else wait_vm_n<0>();
     __syncthreads();  // every wave's part landed; every wave is done with chunk c - 1
-    if (c + 1 < nch) stage(c + 1, (c + 1) & 1);
-    const uint8_t* buf = xs + (c & 1) * kBuf;
+    if (c + NB - 1 < nch) stage(c + NB - 1, (c + NB - 1) % NB);
+    const uint8_t* buf = xs + (c % NB) * kBuf;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int row = 16 * t + r;
@@ -200,16 +202,19 @@ hipError_t launch_t(const int8_t* qx, const float* sx, const int8_t* qw, const f
   // M = 77 17.2 -> 14.2 us, M = 128 23.6 -> 17.6 us); at M <= 16 its chunk
   // barriers cost more than the re-reads they save (7.9 -> 9.4 us at M = 1).
   if (T >= 3 && K % kSmChunk == 0 && K / kSmChunk <= kSmMaxChunks) {
-    constexpr int kLds = 2 * 16 * T * kSmChunk;
+    // three buffers (two chunks in flight) where they fit beside the 1 KB per
+    // tile of int32 sums in the 160 KB of LDS
+    constexpr int NB = 3 * 16 * T * kSmChunk + T * 1024 <= 160 * 1024 ? 3 : 2;
+    constexpr int kLds = NB * 16 * T * kSmChunk;
     static bool configured = false;
     if (!configured) {
-      hipError_t e = hipFuncSetAttribute((const void*)gemm_small_m_lds_kernel<T>,
+      hipError_t e = hipFuncSetAttribute((const void*)gemm_small_m_lds_kernel<T, NB>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
       if (e != hipSuccess) return e;
       configured = true;
     }
-    hipLaunchKernelGGL((gemm_small_m_lds_kernel<T>), dim3((unsigned)grid), dim3(64 * kSmWaves),
-                       kLds, stream, qx, sx, qw, sw, bias, M, N, K, y);
+    hipLaunchKernelGGL((gemm_small_m_lds_kernel<T, NB>), dim3((unsigned)grid),
+                       dim3(64 * kSmWaves), kLds, stream, qx, sx, qw, sw, bias, M, N, K, y);
     return hipGetLastError();
   }
   constexpr int G = T <= 4 ? 8 : 4;
