@@ -31,9 +31,12 @@
  *     weight, T ids): the call then checks its other sizes, enqueues nothing and
  *     returns CONVROT_OK without reading any pointer (they may be NULL).  Every
  *     other size must be positive.
- *   - Arguments are validated on the host before anything is enqueued; on any
- *     error nothing is launched and a negative status is returned.  Faults inside
- *     kernels surface asynchronously on the stream, as for any HIP launch.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     argument error (CONVROT_EINVAL, _ESHAPE, _EWORKSPACE, _EDEVICE) nothing is
+ *     launched.  CONVROT_EHIP reports a failed HIP call or launch; launches of
+ *     the same call made before it (e.g. earlier row chunks) stay enqueued, and
+ *     the outputs are then undefined.  Faults inside kernels surface
+ *     asynchronously on the stream, as for any HIP launch.
  */
 #ifndef CONVROT_H_
 #define CONVROT_H_

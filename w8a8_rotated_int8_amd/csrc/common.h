@@ -4,7 +4,29 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace convrot {
+
+// Raise the dynamic-LDS limit of `n` kernels to bytes[i], once per device (the
+// attribute belongs to the device's copy of the kernel, so a process driving
+// several GPUs sets it on each).  `done` holds one bit per device id below 64;
+// two threads racing on a first call both set the same values, which is
+// harmless.
+inline hipError_t set_lds_limits_once(const void* const* kernels, const int* bytes, int n,
+                                      std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  for (int i = 0; i < n; ++i) {
+    e = hipFuncSetAttribute(kernels[i], hipFuncAttributeMaxDynamicSharedMemorySize, bytes[i]);
+    if (e != hipSuccess) return e;
+  }
+  if (bit) done.fetch_or(bit, std::memory_order_release);
+  return hipSuccess;
+}
 
 constexpr int kWave = 64;
 constexpr int kBlock = 128;  // Hadamard block along the contraction axis

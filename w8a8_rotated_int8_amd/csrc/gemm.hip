@@ -828,12 +828,11 @@ hipError_t launch(const GemmArgs& a, hipStream_t stream) {
   constexpr int kLds = STAGES * 2 * kTile * BK + (EPI == kEpiDequantLoraBf16 ? 2 * kTile * 64 : 0) +
                        (EPI == kEpiDequantBf16 && !PT ? kTile * 4 : 0);
   auto kern = gemm_kernel<EPI, PT, BF16, WI, WJ, BK, STAGES>;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  {
+    static std::atomic<uint64_t> configured{0};
+    const void* k = (const void*)kern;
+    hipError_t e = set_lds_limits_once(&k, &kLds, 1, configured);
     if (e != hipSuccess) return e;
-    configured = true;
   }
   const int64_t gi = (a.I + kTile - 1) / kTile, gj = (a.J + kTile - 1) / kTile;
   if (gi <= 0 || gj <= 0) return hipSuccess;
@@ -868,11 +867,11 @@ hipError_t launch_gemm_i8_splitk_dequant(const GemmArgs& a, int S, int32_t* part
   if (S < 1 || a.Kc % (S * kBK) || a.I % 4) return hipErrorInvalidValue;
   constexpr int kLds = kStages * 2 * kTile * kBK;
   auto kern = gemm_splitk_kernel<kWI, kWJ, kBK, kStages>;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  {
+    static std::atomic<uint64_t> configured{0};
+    const void* k = (const void*)kern;
+    hipError_t e = set_lds_limits_once(&k, &kLds, 1, configured);
     if (e != hipSuccess) return e;
-    configured = true;
   }
   const int64_t gi = (a.I + kTile - 1) / kTile, gj = (a.J + kTile - 1) / kTile;
   const int64_t tiles = gi * gj;

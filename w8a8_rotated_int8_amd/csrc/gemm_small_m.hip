@@ -206,13 +206,10 @@ hipError_t launch_t(const int8_t* qx, const float* sx, const int8_t* qw, const f
     // tile of int32 sums in the 160 KB of LDS
     constexpr int NB = 3 * 16 * T * kSmChunk + T * 1024 <= 160 * 1024 ? 3 : 2;
     constexpr int kLds = NB * 16 * T * kSmChunk;
-    static bool configured = false;
-    if (!configured) {
-      hipError_t e = hipFuncSetAttribute((const void*)gemm_small_m_lds_kernel<T, NB>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-      if (e != hipSuccess) return e;
-      configured = true;
-    }
+    static std::atomic<uint64_t> configured{0};
+    const void* k = (const void*)gemm_small_m_lds_kernel<T, NB>;
+    hipError_t e = set_lds_limits_once(&k, &kLds, 1, configured);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemm_small_m_lds_kernel<T, NB>), dim3((unsigned)grid),
                        dim3(64 * kSmWaves), kLds, stream, qx, sx, qw, sw, bias, M, N, K, y);
     return hipGetLastError();

@@ -108,9 +108,8 @@ hipError_t launch_rotate_quant(const uint16_t* x, int64_t rows, int K, int8_t* q
   // waves per CU, ran 5% slower than reading the scales from global memory).
   constexpr int kMaxCslWaves = 12;
   constexpr int kLdsPerCu = 160 * 1024;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipSuccess;
+  {
+    static std::atomic<uint64_t> configured{0};
     const int max_lds = CONVROT_MAX_ROW_LEN_BLOCKS * 256;
     const void* ks[4] = {(const void*)rotate_quant_long_kernel<kRotate, kSpan, false, false>,
                          (const void*)rotate_quant_long_kernel<kRotate, kSpan, false, true>,
@@ -118,11 +117,8 @@ hipError_t launch_rotate_quant(const uint16_t* x, int64_t rows, int K, int8_t* q
                          (const void*)rotate_quant_long_kernel<kFold, kSpan, true, false>};
     const int lim[4] = {max_lds, max_lds, max_lds,
                         kMaxCslWaves * (span_bytes<kSpan>() + kSpan * 512)};
-    for (int k = 0; k < 4; ++k) {
-      e = hipFuncSetAttribute(ks[k], hipFuncAttributeMaxDynamicSharedMemorySize, lim[k]);
-      if (e != hipSuccess) return e;
-    }
-    configured = true;
+    hipError_t e = set_lds_limits_once(ks, lim, 4, configured);
+    if (e != hipSuccess) return e;
   }
   if (K / kBlock < kSpan) {
     const int64_t tasks = (rows + pl.rows_per_wave - 1) / pl.rows_per_wave;
