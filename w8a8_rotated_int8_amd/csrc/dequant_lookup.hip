@@ -260,13 +260,10 @@ hipError_t launch_embedding_lookup(const int32_t* ids, int64_t T, const int8_t* 
                                    int32_t* oob, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   if (D <= 4096) {
-    static int n_cu = 0;
-    if (n_cu == 0) {
-      int dev = 0;
-      hipError_t e = hipGetDevice(&dev);
-      if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-      if (e != hipSuccess) return e;
-    }
+    int dev = 0, n_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
     int64_t grid = (T + 3) / 4;
     const int64_t cap = 4 * (int64_t)n_cu;  // four resident workgroups per CU
     if (grid > cap) grid = cap;
