@@ -159,7 +159,6 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("" ::: "memory");
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // 32-bit LDS address of a pointer into __shared__ memory.
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
@@ -212,9 +211,5 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
                : "memory", "m0");
 }
 
-// 16-byte direct global->LDS load: lane i's 16 bytes land at lds_base + 16*i.
-__device__ __forceinline__ void load_lds_16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
-}
 
 }  // namespace convrot

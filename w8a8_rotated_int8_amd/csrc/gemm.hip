@@ -8,7 +8,8 @@
 //   forward:         P = q_w [N, K], Q = q_x [M, K]; y[m][n] =
 //                    bf16(fl32(acc) * s_x[m] * s_w[n] (+ bias[n]))
 //   int8 grad_x:     P = q_w read as [N, K] but contracted along its rows
-//                    (transposed in registers), Q = q_g [M, N]; the epilogue
+//                    (staged as is, transposed by the LDS reads), Q = q_g
+//                    [M, N]; the epilogue
 //                    scales by s_g[m] and applies the inverse rotation along k
 //                    inside each 128-block (one wave owns whole blocks)
 //   raw int32:       test and timing hook
@@ -49,6 +50,7 @@
 #define CONVROT_GEMM_GROUP_J 4
 #endif
 
+
 namespace convrot {
 namespace {
 
@@ -56,6 +58,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int kTile = 256;
 constexpr int kNumXcd = 8;
@@ -108,103 +113,6 @@ __device__ __forceinline__ void wait_stages(int later) {
 // Callers wait explicitly for the data they need before it.
 __device__ __forceinline__ void raw_barrier() {
   asm volatile("s_barrier" ::: "memory");
-}
-
-// Stage rows [row0, row0 + 256) x bytes [kb0, kb0 + BK) of a row-major operand
-// into an LDS buffer of 256 rows x BK bytes.  Rows past the end are clamped to
-// the last row (their results are discarded).  NT threads; each DMA
-// instruction fills 1 KB of LDS.
-template <int BK, int NT>
-__device__ __forceinline__ void stage_rows(const uint8_t* base, int64_t ld_bytes, int64_t row0,
-                                           int64_t nrows, int64_t kb0, uint8_t* lds_stage,
-                                           int tid) {
-  constexpr int kChunks = BK / 16;
-  constexpr int kIters = kTile * kChunks / NT;
-  const int wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int blk = it * (NT / 64) + wave;  // 1 KB block of the stage
-    const int slot = blk * 64 + lane;
-    const int row = slot / kChunks;
-    const int chunk = (slot % kChunks) ^ swz<BK>(row);
-    int64_t gr = row0 + row;
-    gr = gr < nrows ? gr : nrows - 1;
-    dma16(base + gr * ld_bytes + kb0 + 16 * chunk,
-          __builtin_amdgcn_readfirstlane(lds_u32(lds_stage) + blk * 1024));
-  }
-}
-
-// 4 x 4 byte transpose: out[c] byte r = in[r] byte c.
-__device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
-                                             uint32_t& o0, uint32_t& o1, uint32_t& o2,
-                                             uint32_t& o3) {
-  uint32_t t0 = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
-  uint32_t t1 = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
-  uint32_t u0 = __builtin_amdgcn_perm(d, c, 0x05010400u);  // c0 d0 c1 d1
-  uint32_t u1 = __builtin_amdgcn_perm(d, c, 0x07030602u);  // c2 d2 c3 d3
-  o0 = __builtin_amdgcn_perm(u0, t0, 0x05040100u);         // a0 b0 c0 d0
-  o1 = __builtin_amdgcn_perm(u0, t0, 0x07060302u);         // a1 b1 c1 d1
-  o2 = __builtin_amdgcn_perm(u1, t1, 0x05040100u);         // a2 b2 c2 d2
-  o3 = __builtin_amdgcn_perm(u1, t1, 0x07060302u);         // a3 b3 c3 d3
-}
-
-// Transposed int8 operand (BK = 128): source [Kc, I] (I contiguous).  The
-// NT / 32 groups of 32 lanes split the stage's 128 k rows, RP = 4096 / NT rows
-// each; lane ic of a group loads an RP (k) x 8 (i) byte block with 8-byte
-// loads (32 lanes cover the 256 i of the tile), transposes it in registers
-// (v_perm) and writes 8 LDS rows (one per i) of RP k-bytes each.
-template <int NT>
-struct TransposedRegs {
-  static constexpr int RP = 128 * 32 / NT;
-  uint2 r[RP];
-};
-
-template <int NT>
-__device__ __forceinline__ void load_transposed(const int8_t* src, int64_t ld, int64_t I,
-                                                int64_t i0, int64_t k0, int tid,
-                                                TransposedRegs<NT>& t) {
-  constexpr int RP = TransposedRegs<NT>::RP;
-  const int ic = tid & 31, kg = tid >> 5;
-  int64_t i = i0 + 8 * ic;
-  i = i + 8 <= I ? i : I - 8;
-  const int8_t* p = src + (k0 + RP * kg) * ld + i;
-#pragma unroll
-  for (int r = 0; r < RP; ++r) t.r[r] = *reinterpret_cast<const uint2*>(p + r * ld);
-}
-
-// Half `hf` of the transposed write: columns i = 8 ic + 4 hf .. + 3 (the .x
-// or .y bytes of the loaded rows).
-template <int NT>
-__device__ __forceinline__ void store_transposed_half(const TransposedRegs<NT>& t,
-                                                      uint8_t* lds_stage, int tid, int hf) {
-  constexpr int RP = TransposedRegs<NT>::RP;
-  static_assert(RP == 8 || RP == 16, "8 or 16 k rows per lane");
-  const int ic = tid & 31, kg = tid >> 5;
-  uint32_t o[4][RP / 4];  // o[j][d]: bytes (k = 4d .. 4d+3 of the lane's rows) of column 8 ic + 4 hf + j
-#pragma unroll
-  for (int d = 0; d < RP / 4; ++d) {
-    if (hf == 0)
-      transpose4x4(t.r[4 * d].x, t.r[4 * d + 1].x, t.r[4 * d + 2].x, t.r[4 * d + 3].x, o[0][d],
-                   o[1][d], o[2][d], o[3][d]);
-    else
-      transpose4x4(t.r[4 * d].y, t.r[4 * d + 1].y, t.r[4 * d + 2].y, t.r[4 * d + 3].y, o[0][d],
-                   o[1][d], o[2][d], o[3][d]);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint8_t* dst = lds_stage + lds_off<128>(8 * ic + 4 * hf + j, (RP * kg) >> 4) + ((RP * kg) & 15);
-    if constexpr (RP == 16)
-      *reinterpret_cast<uint4*>(dst) = make_uint4(o[j][0], o[j][1], o[j][2], o[j][3]);
-    else
-      *reinterpret_cast<uint2*>(dst) = make_uint2(o[j][0], o[j][1]);
-  }
-}
-
-template <int NT>
-__device__ __forceinline__ void store_transposed(const TransposedRegs<NT>& t, uint8_t* lds_stage,
-                                                 int tid) {
-  store_transposed_half<NT>(t, lds_stage, tid, 0);
-  store_transposed_half<NT>(t, lds_stage, tid, 1);
 }
 
 // Dispatch id -> (i tile, j tile), XCD-aware (see the file comment).
@@ -354,136 +262,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
 #pragma unroll
     for (int y = 0; y < NJ; ++y) acc[x][y] = acc_t{};
 
-  auto issue_stage = [&](int kt, int buf) {
-    const int64_t kb = (int64_t)kt * BK;
-    stage_rows<BK, NT>(P, a.ldp * esz, i0, a.I, kb, Ps(buf), tid);
-    stage_rows<BK, NT>(Q, a.ldq * esz, j0, a.J, kb, Qs(buf), tid);
-  };
-
-  auto compute_stage = [&](int buf) {
-    const uint8_t* ps = Ps(buf);
-    const uint8_t* qs = Qs(buf);
-#pragma unroll
-    for (int s = 0; s < BK / 32; ++s) {
-      uint4 pf[NI], qf[NJ];
-      const int chunk = 2 * s + (lane >> 5);
-#pragma unroll
-      for (int t = 0; t < NI; ++t)
-        pf[t] = *reinterpret_cast<const uint4*>(ps + lds_off<BK>(wi * TI + t * 32 + (lane & 31), chunk));
-#pragma unroll
-      for (int t = 0; t < NJ; ++t)
-        qf[t] = *reinterpret_cast<const uint4*>(qs + lds_off<BK>(wj * TJ + t * 32 + (lane & 31), chunk));
-#pragma unroll
-      for (int x = 0; x < NI; ++x)
-#pragma unroll
-        for (int y = 0; y < NJ; ++y) acc[x][y] = mfma(pf[x], qf[y], acc[x][y]);
-    }
-  };
-
-  if constexpr (PT) {
-    // Transposed P (the int8 input gradient): P's stage block arrives in
-    // registers one stage ahead (16 eight-byte loads per thread) and is
-    // transposed into LDS in two halves, each interleaved with the MFMAs of one
-    // slice of the current stage; Q arrives by direct loads.  As in the
-    // row-major case, the fragment reads of slice s + 1 are interleaved with
-    // the MFMAs of slice s, and the last stage is peeled.
-    static_assert(BK / 32 == 4, "transposed P: 4 slices per stage");
-    constexpr int kQLoads = kTile * (BK / 16) / NT;  // Q direct loads per thread per stage
-    const int8_t* Pt = static_cast<const int8_t*>(a.P);
-    TransposedRegs<NT> tr;
-    uint4 F[2][NI + NJ];
-    auto read_frags = [&](int buf, int s, uint4* f) {
-      const uint8_t* ps = Ps(buf);
-      const uint8_t* qs = Qs(buf);
-      const int chunk = 2 * s + (lane >> 5);
-#pragma unroll
-      for (int t = 0; t < NI; ++t)
-        f[t] = *reinterpret_cast<const uint4*>(ps + lds_off<BK>(wi * TI + t * 32 + (lane & 31), chunk));
-#pragma unroll
-      for (int t = 0; t < NJ; ++t)
-        f[NI + t] = *reinterpret_cast<const uint4*>(qs + lds_off<BK>(wj * TJ + t * 32 + (lane & 31), chunk));
-    };
-    // MFMAs of slice s with, spread over them: the next slice's fragment
-    // reads (issued just before, one per MFMA from the first), NV VALU
-    // operations (the transposes of a half, evenly) and ND LDS writes (its
-    // results, on the last MFMAs).
-    auto mfma_slice = [&](int s, auto nv, auto nd) {
-      constexpr int NV = decltype(nv)::value, ND = decltype(nd)::value;
-      constexpr int NM = NI * NJ;
-#pragma unroll
-      for (int x = 0; x < NI; ++x)
-#pragma unroll
-        for (int y = 0; y < NJ; ++y) acc[x][y] = mfma(F[s & 1][x], F[s & 1][NI + y], acc[x][y]);
-#pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        if (i < NI + NJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // one MFMA
-        if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV / NM, 0);  // VALU
-        if (ND > 0 && i >= NM - ND) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    using Z = std::integral_constant<int, 0>;
-    using VH = std::integral_constant<int, 2 * TransposedRegs<NT>::RP>;  // v_perm per half
-    using D4 = std::integral_constant<int, 4>;                           // LDS writes per half
-
-    stage_rows<BK, NT>(Q, a.ldq * esz, j0, a.J, 0, Qs(0), tid);
-    load_transposed(Pt, a.ldp, a.I, i0, 0, tid, tr);
-    store_transposed<NT>(tr, Ps(0), tid);
-    if (nk > 1) {
-      stage_rows<BK, NT>(Q, a.ldq * esz, j0, a.J, BK, Qs(1), tid);
-      load_transposed(Pt, a.ldp, a.I, i0, BK, tid, tr);
-      wait_vm<kQLoads + TransposedRegs<NT>::RP>();  // stage 0's Q loads (the oldest) have landed
-    } else {
-      wait_vm<0>();
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's P writes landed
-    raw_barrier();
-    read_frags(0, 0, F[0]);
-    auto stage = [&](int kt, auto has_next) {
-      constexpr bool HAS_NEXT = decltype(has_next)::value;
-      const int buf = kt & 1;
-      // slice 0
-      read_frags(buf, 1, F[1]);
-      mfma_slice(0, Z{}, Z{});
-      // slices 1 and 2: transpose the next stage's P into the other buffer
-      read_frags(buf, 2, F[0]);
-      if constexpr (HAS_NEXT) {
-        store_transposed_half<NT>(tr, Ps(buf ^ 1), tid, 0);
-        mfma_slice(1, VH{}, D4{});
-      } else {
-        mfma_slice(1, Z{}, Z{});
-      }
-      read_frags(buf, 3, F[1]);
-      if constexpr (HAS_NEXT) {
-        store_transposed_half<NT>(tr, Ps(buf ^ 1), tid, 1);
-        mfma_slice(2, VH{}, D4{});
-        // publish stage kt + 1: its Q loads have landed and every wave's P
-        // writes are done; then start stage kt + 2's loads
-        wait_vm<0>();
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        raw_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(buf ^ 1, 0, F[0]);
-        mfma_slice(3, Z{}, Z{});
-        if (kt + 2 < nk) {
-          const int64_t kb = (int64_t)(kt + 2) * BK;
-          stage_rows<BK, NT>(Q, a.ldq * esz, j0, a.J, kb, Qs(buf), tid);
-          load_transposed(Pt, a.ldp, a.I, i0, kb, tid, tr);
-        }
-      } else {
-        mfma_slice(2, Z{}, Z{});
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int x = 0; x < NI; ++x)
-#pragma unroll
-          for (int y = 0; y < NJ; ++y) acc[x][y] = mfma(F[1][x], F[1][NI + y], acc[x][y]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, std::true_type{});
-    if (nk > 0) stage(nk - 1, std::false_type{});
-  } else {
+  // The transposed P of the int8 input gradient (q_w read as [k][i]) is
+  // staged in its natural layout and transposed by the LDS reads.
+  constexpr bool TR = PT;
+  {
     // Per-thread source pointers and LDS destinations of the stage loads,
     // computed once: a stage load is then one 64-bit add per instruction.
     constexpr int kRowDma = kTile * (BK / 16) / NT;  // per operand per stage
@@ -495,6 +277,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
       for (int it = 0; it < kRowDma; ++it) {
         const int blk = it * (NT / 64) + wave;
         const int slot = blk * 64 + lane;
+        if (TR && op == 0) {
+          // P in its natural layout [k][i]: the stage holds BK k-rows of the
+          // tile's 256 i-bytes; 16-byte position q of row n holds piece
+          // q ^ 2 (n & 7).  A 32-lane half of a transpose read touches 8 rows
+          // and two adjacent pieces (an even one and the next), which then
+          // land in 16 different positions: no bank conflicts.
+          const int n = slot >> 4, q = slot & 15;
+          int64_t col = i0 + 16 * (q ^ (2 * (n & 7)));
+          col = col + 16 <= a.I ? col : a.I - 16;  // columns past the end: valid, unused
+          src[it] = P + (int64_t)n * a.ldp + col;
+          dst_off[it] = blk * 1024;
+          continue;
+        }
         const int row = slot / (BK / 16);
         const int chunk = (slot % (BK / 16)) ^ swz<BK>(row);
         const int64_t row0 = op ? j0 : i0, nrows = op ? a.J : a.I;
@@ -507,9 +302,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
     const uint32_t lds_base = lds_u32(lds);
     auto issue = [&](int kt, int buf) {
       const int64_t kb = (int64_t)kt * BK;
+      const int64_t kbp = TR ? kb * a.ldp : kb;  // P advances by rows when it is [k][i]
       const uint32_t b0 = lds_base + buf * 2 * kStage;
 #pragma unroll
-      for (int d = 0; d < 2 * kRowDma; ++d) dma16(src[d] + kb, b0 + dst_off[d]);
+      for (int d = 0; d < 2 * kRowDma; ++d) dma16(src[d] + (d < kRowDma ? kbp : kb), b0 + dst_off[d]);
     };
     constexpr int SL = BK / 32;
     static_assert(SL % 2 == 0, "fragment double buffer alternates per slice");
@@ -518,9 +314,32 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
       const uint8_t* ps = Ps(buf);
       const uint8_t* qs = Qs(buf);
       const int chunk = 2 * s + (lane >> 5);
+      if constexpr (TR) {
+        // ds_read_b64_tr_b8: in each 16-lane group, lane j < 8 receives byte j
+        // of the 8-byte rows addressed by the group's even lanes, lane j >= 8
+        // byte j - 8 of those of its odd lanes.  Even lane 2m and odd lane
+        // 2m + 1 address k-row n0 + m at i-offsets +0 and +8, so lane j gets
+        // k-rows n0 .. n0 + 7 of output row i = base + j: two reads (n0 and
+        // n0 + 8) give the 16 k-contiguous bytes of the MFMA's A operand,
+        // the same layout as the row-major path.
+        const lds_u8* ps3 = (const lds_u8*)ps;
+        const int a16 = lane & 15;
+        const int n0 = 32 * s + 16 * (lane >> 5) + (a16 >> 1);
 #pragma unroll
-      for (int t = 0; t < NI; ++t)
-        f[t] = *reinterpret_cast<const uint4*>(ps + lds_off<BK>(wi * TI + t * 32 + (lane & 31), chunk));
+        for (int t = 0; t < NI; ++t) {
+          const int ib = wi * TI + t * 32 + 16 * ((lane >> 4) & 1) + 8 * (a16 & 1);
+          const int pc = ib >> 4, hb = 8 * (a16 & 1);
+          const int pos = 16 * (pc ^ (2 * (n0 & 7))) + hb;  // rows n0 and n0 + 8 alike
+          const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(ps3 + n0 * 256 + pos));
+          const v2i hi =
+              __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(ps3 + (n0 + 8) * 256 + pos));
+          f[t] = make_uint4((uint32_t)lo.x, (uint32_t)lo.y, (uint32_t)hi.x, (uint32_t)hi.y);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < NI; ++t)
+          f[t] = *reinterpret_cast<const uint4*>(ps + lds_off<BK>(wi * TI + t * 32 + (lane & 31), chunk));
+      }
 #pragma unroll
       for (int t = 0; t < NJ; ++t)
         f[NI + t] = *reinterpret_cast<const uint4*>(qs + lds_off<BK>(wj * TJ + t * 32 + (lane & 31), chunk));
@@ -558,12 +377,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
       for (int x = 0; x < NI; ++x)
 #pragma unroll
         for (int y = 0; y < NJ; ++y) acc[x][y] = mfma(F[s & 1][x], F[s & 1][NI + y], acc[x][y]);
+      // a transposed P fragment takes two 8-byte transpose reads
+      constexpr int NR = (TR ? 2 : 1) * NI + NJ, NM = NI * NJ;
+      constexpr int NP = NR < NM ? NR : NM;
 #pragma unroll
-      for (int i = 0; i < NI + NJ; ++i) {
+      for (int i = 0; i < NP; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, NI * NJ - (NI + NJ), 0);
+      if constexpr (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
+      if constexpr (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
       __builtin_amdgcn_sched_barrier(0);
     };
     // One stage.  HAS_NEXT is a compile-time flag (the final stage is peeled
@@ -848,8 +671,8 @@ constexpr int kBK = CONVROT_GEMM_BK, kStages = CONVROT_GEMM_STAGES;
 
 hipError_t launch_gemm_i8(const GemmArgs& a, int epilogue, bool p_transposed, hipStream_t stream) {
   if (p_transposed) {
-    if (epilogue == kEpiI32) return launch<kEpiI32, true, false, 2, 2, 128, 2>(a, stream);
-    if (epilogue == kEpiInvRotBf16) return launch<kEpiInvRotBf16, true, false, 2, 2, 128, 2>(a, stream);
+    if (epilogue == kEpiI32) return launch<kEpiI32, true, false, 2, 4, 128, 2>(a, stream);
+    if (epilogue == kEpiInvRotBf16) return launch<kEpiInvRotBf16, true, false, 2, 4, 128, 2>(a, stream);
     return hipErrorInvalidValue;
   }
   if (epilogue == kEpiI32) return launch<kEpiI32, false, false, kWI, kWJ, kBK, kStages>(a, stream);
