@@ -1,10 +1,13 @@
 """Text-encoder shapes: one caption at a time (small, ragged M) and skinny
 outputs (N = 32), as in the training guide's text-encoder quantization
 (section 7.1, text encoder bullet).  With few 256 x 256 output tiles the
-forward either runs the few-row kernel (M <= 128, N = 2048..8192, K <= 8192:
-16 output columns per workgroup, the waves' int32 sums added in LDS) or
-splits the contraction (split-K) into int32 partials that one more launch sums
-and dequantizes.
+forward runs one of three paths:
+  * the few-row kernel (M <= 128, N = 2048..8192, K <= 8192): 16 output columns
+    per workgroup, the waves' int32 sums added in LDS;
+  * the same kernel with the roles swapped for few output columns over many
+    tokens (N <= 128, M >= 2048): 16 tokens per workgroup;
+  * split-K: the contraction split into int32 partials that one more launch
+    sums and dequantizes.
 
   * either forward equals the one-pass stages (quantize_act + the int8 GEMM
     with its dequantizing epilogue) bit for bit: integer sums are exact and the
@@ -38,7 +41,11 @@ def cr():
 SHAPES = [(1, 4096, 4096), (7, 4096, 4096), (77, 4096, 4096), (128, 4096, 4096),
           (33, 4096, 3000), (16, 8192, 2048), (100, 8192, 4096), (300, 4096, 4096),
           (64, 4096, 4096), (90, 4096, 2048), (110, 2048, 4096), (47, 1024, 2048),
-          (77, 4096, 12288), (77, 12288, 4096), (77, 4096, 32), (4096, 4096, 32), (129, 512, 640)]
+          (77, 4096, 12288), (77, 12288, 4096), (77, 4096, 32), (4096, 4096, 32), (129, 512, 640),
+          # few output columns over many tokens (the roles swapped): tile counts
+          # ceil(N / 16) = 1, 3 (LDS), 7 (ragged, LDS) and 8 (LDS); K = 8192 direct
+          (2048, 4096, 16), (4096, 2048, 48), (3000, 1024, 100), (2048, 4096, 128),
+          (2500, 8192, 24)]
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
@@ -67,8 +74,8 @@ def test_small_m_forward(cr, M, K, N):
     print(f"  max row relerr {e:.2e}", flush=True)
 
 
-def test_small_m_with_bias(cr):
-    M, K, N = 77, 4096, 4096
+@pytest.mark.parametrize("M,K,N", [(77, 4096, 4096), (4096, 4096, 32), (2048, 2048, 100)])
+def test_small_m_with_bias(cr, M, K, N):
     x = wl.activations(M, K, wl.n_outliers(K), base=1)
     w = wl.packed_weight(4100, 1, N, K)
     bias = bf16_to_dev(wl.normal_bf16((N,), 1.0, 1, 18))

@@ -150,7 +150,7 @@ int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw
   float* sx = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + align256((size_t)M * K));
   hipError_t e = launch_rotate_quant(x, M, (int)K, qx, sx, nullptr, false, false, stream);
   if (e != hipSuccess) return CONVROT_EHIP;
-  if (use_small_m(M, N, K))
+  if (small_m_mode(M, N, K))
     return hip_status(launch_gemm_small_m(qx, sx, qw, sw, bias, M, N, K, y, stream));
   GemmArgs a{};
   a.P = qw; a.Q = qx; a.I = N; a.J = M; a.Kc = K; a.ldp = K; a.ldq = K;

@@ -718,7 +718,7 @@ int splitk_factor(int64_t M, int64_t N, int64_t K) {
   // contraction byte of one tile, measured), plus writing and reading the
   // int32 partials at ~5 TB/s.  S = 1 keeps the one-pass GEMM.
   const int64_t tiles = ((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile);
-  if (tiles >= 128 || N % 4 || use_small_m(M, N, K)) return 1;
+  if (tiles >= 128 || N % 4 || small_m_mode(M, N, K)) return 1;
   const int64_t kb = K / kBlock;
   int best = 1;
   double best_t = 0.0;

@@ -27,8 +27,34 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kSmWaves = 8;
 
+// Output element (m, nn) of the contraction of the few rows (m < M) with the
+// many (nn < N).  Plain: the few rows are q_x's (tokens), the many q_w's, and
+// y[m][nn] = bf16(fl32(fl32(float(acc) * s_x[m]) * s_w[nn]) (+ bias[nn])).
+// Swapped (SW, few output columns): the few rows are q_w's and the many q_x's,
+// with sx / sw / M / N passed in those roles; the same operations in the same
+// order give y[nn][m] = bf16(fl32(fl32(float(acc) * s_x[nn]) * s_w[m]) (+ bias[m])).
+template <bool SW>
+__device__ __forceinline__ void store_out(int32_t acc, int64_t m, int64_t nn, int64_t M,
+                                          int64_t N, const float* __restrict__ sx,
+                                          const float* __restrict__ sw,
+                                          const uint16_t* __restrict__ bias,
+                                          uint16_t* __restrict__ y) {
+  float f = (float)acc;
+  if constexpr (SW) {
+    f = f * sw[nn];
+    f = f * sx[m];
+    if (bias) f = f + __uint_as_float((uint32_t)bias[m] << 16);
+    y[nn * M + m] = (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu);
+  } else {
+    f = f * sx[m];
+    f = f * sw[nn];
+    if (bias) f = f + __uint_as_float((uint32_t)bias[nn] << 16);
+    y[m * N + nn] = (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu);
+  }
+}
+
 // T: 16-row tiles of q_x (M <= 16 T); G: 64-wide k-steps per load group.
-template <int T, int G>
+template <int T, int G, bool SW>
 __global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_kernel(
     const int8_t* __restrict__ qx, const float* __restrict__ sx, const int8_t* __restrict__ qw,
     const float* __restrict__ sw, const uint16_t* __restrict__ bias, int64_t M, int64_t N,
@@ -83,13 +109,7 @@ __global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_kernel(
     const int l = idx & 63, v = (idx >> 6) & 3, t = idx >> 8;
     const int64_t m = 16 * t + 4 * (l >> 4) + v;
     const int64_t nn = n0 + (l & 15);
-    if (m < M && nn < N) {
-      float f = (float)part[t][v][l];
-      f = f * sx[m];
-      f = f * sw[nn];
-      if (bias) f = f + __uint_as_float((uint32_t)bias[nn] << 16);
-      y[m * N + nn] = (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu);
-    }
+    if (m < M && nn < N) store_out<SW>(part[t][v][l], m, nn, M, N, sx, sw, bias, y);
   }
 }
 
@@ -108,7 +128,7 @@ __global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_kernel(
 constexpr int kSmChunk = 512;
 constexpr int kSmMaxChunks = 8;
 
-template <int T, int NB>
+template <int T, int NB, bool SW>
 __global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_lds_kernel(
     const int8_t* __restrict__ qx, const float* __restrict__ sx, const int8_t* __restrict__ qw,
     const float* __restrict__ sw, const uint16_t* __restrict__ bias, int64_t M, int64_t N,
@@ -183,17 +203,13 @@ __global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_lds_kernel(
     const int l = idx & 63, v = (idx >> 6) & 3, t = idx >> 8;
     const int64_t m = 16 * t + 4 * (l >> 4) + v;
     const int64_t nn = n0 + (l & 15);
-    if (m < M && nn < N) {
-      float f = (float)part[t][v][l];
-      f = f * sx[m];
-      f = f * sw[nn];
-      if (bias) f = f + __uint_as_float((uint32_t)bias[nn] << 16);
-      y[m * N + nn] = (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu);
-    }
+    if (m < M && nn < N) store_out<SW>(part[t][v][l], m, nn, M, N, sx, sw, bias, y);
   }
 }
 
-template <int T>
+// In kernel terms: M few rows (qx, sx), N many (qw, sw); SW when the few are
+// the weight's rows (see store_out).
+template <int T, bool SW>
 hipError_t launch_t(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw,
                     const uint16_t* bias, int64_t M, int64_t N, int64_t K, uint16_t* y,
                     hipStream_t stream) {
@@ -207,44 +223,57 @@ hipError_t launch_t(const int8_t* qx, const float* sx, const int8_t* qw, const f
     constexpr int NB = 3 * 16 * T * kSmChunk + T * 1024 <= 160 * 1024 ? 3 : 2;
     constexpr int kLds = NB * 16 * T * kSmChunk;
     static std::atomic<uint64_t> configured{0};
-    const void* k = (const void*)gemm_small_m_lds_kernel<T, NB>;
+    const void* k = (const void*)gemm_small_m_lds_kernel<T, NB, SW>;
     hipError_t e = set_lds_limits_once(&k, &kLds, 1, configured);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_small_m_lds_kernel<T, NB>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((gemm_small_m_lds_kernel<T, NB, SW>), dim3((unsigned)grid),
                        dim3(64 * kSmWaves), kLds, stream, qx, sx, qw, sw, bias, M, N, K, y);
     return hipGetLastError();
   }
   constexpr int G = T <= 4 ? 8 : 4;
-  hipLaunchKernelGGL((gemm_small_m_kernel<T, G>), dim3((unsigned)grid), dim3(64 * kSmWaves), 0,
-                     stream, qx, sx, qw, sw, bias, M, N, K, y);
+  hipLaunchKernelGGL((gemm_small_m_kernel<T, G, SW>), dim3((unsigned)grid), dim3(64 * kSmWaves),
+                     0, stream, qx, sx, qw, sw, bias, M, N, K, y);
   return hipGetLastError();
+}
+
+template <bool SW>
+hipError_t launch_few(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw,
+                      const uint16_t* bias, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                      hipStream_t stream) {
+  switch ((M + 15) / 16) {
+    case 1: return launch_t<1, SW>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+    case 2: return launch_t<2, SW>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+    case 3: return launch_t<3, SW>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+    case 4: return launch_t<4, SW>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+    case 5: return launch_t<5, SW>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+    case 6: return launch_t<6, SW>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+    case 7: return launch_t<7, SW>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+    default: return launch_t<8, SW>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+  }
 }
 
 }  // namespace
 
-bool use_small_m(int64_t M, int64_t N, int64_t K) {
+int small_m_mode(int64_t M, int64_t N, int64_t K) {
+  if (K % 64 || K > 8192) return 0;
   // Measured against split-K (forward, M = 1..128): faster for N = 2048..4096
   // at K = 4096; with N >= 12288 the per-workgroup re-reads of q_x (768
   // workgroups) and with K = 12288 the 8-way K split per workgroup lose.
-  return M >= 1 && M <= kSmallM && K % 64 == 0 && K <= 8192 && N >= 2048 && N <= 8192;
+  if (M >= 1 && M <= kSmallM && N >= 2048 && N <= 8192) return 1;
+  // Few output columns (a skinny weight) over many tokens: the same kernel
+  // with the roles swapped, each workgroup reading 16 token rows once.
+  if (N >= 1 && N <= kSmallM && M >= 2048 && M <= 0x7ffffff0) return 2;
+  return 0;
 }
 
 hipError_t launch_gemm_small_m(const int8_t* qx, const float* sx, const int8_t* qw,
                                const float* sw, const uint16_t* bias, int64_t M, int64_t N,
                                int64_t K, uint16_t* y, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (M > kSmallM || K % 64 || K / 64 > 0x7fffffff || (N + 15) / 16 > 0x7fffffff)
-    return hipErrorInvalidValue;
-  switch ((M + 15) / 16) {
-    case 1: return launch_t<1>(qx, sx, qw, sw, bias, M, N, K, y, stream);
-    case 2: return launch_t<2>(qx, sx, qw, sw, bias, M, N, K, y, stream);
-    case 3: return launch_t<3>(qx, sx, qw, sw, bias, M, N, K, y, stream);
-    case 4: return launch_t<4>(qx, sx, qw, sw, bias, M, N, K, y, stream);
-    case 5: return launch_t<5>(qx, sx, qw, sw, bias, M, N, K, y, stream);
-    case 6: return launch_t<6>(qx, sx, qw, sw, bias, M, N, K, y, stream);
-    case 7: return launch_t<7>(qx, sx, qw, sw, bias, M, N, K, y, stream);
-    default: return launch_t<8>(qx, sx, qw, sw, bias, M, N, K, y, stream);
-  }
+  const int mode = small_m_mode(M, N, K);
+  if (mode == 1) return launch_few<false>(qx, sx, qw, sw, bias, M, N, K, y, stream);
+  if (mode == 2) return launch_few<true>(qw, sw, qx, sx, bias, N, M, K, y, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace convrot

@@ -62,10 +62,11 @@ hipError_t launch_gemm_i8_splitk_dequant(const GemmArgs& a, int S, int32_t* part
 // Split count for a forward of M tokens, N outputs, K inputs (1 = no split).
 int splitk_factor(int64_t M, int64_t N, int64_t K);
 
-// Forward contraction + dequantization for at most kSmallM activation rows
-// (gemm_small_m.hip); use_small_m says when the forward takes it.
+// Forward contraction + dequantization for at most kSmallM activation rows, or
+// at most kSmallM output columns over many rows (gemm_small_m.hip);
+// small_m_mode says when the forward takes it (0: it does not).
 constexpr int64_t kSmallM = 128;
-bool use_small_m(int64_t M, int64_t N, int64_t K);
+int small_m_mode(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_small_m(const int8_t* qx, const float* sx, const int8_t* qw,
                                const float* sw, const uint16_t* bias, int64_t M, int64_t N,
                                int64_t K, uint16_t* y, hipStream_t stream);
