@@ -2,8 +2,8 @@
 outputs (N = 32), as in the training guide's text-encoder quantization
 (section 7.1, text encoder bullet).  With few 256 x 256 output tiles the
 forward runs one of three paths:
-  * the few-row kernel (M <= 128, N = 2048..8192, K <= 8192): 16 output columns
-    per workgroup, the waves' int32 sums added in LDS;
+  * the few-row kernel (M <= 128, N <= 8192, K <= 8192): 16 output columns per
+    workgroup, the waves' int32 sums added in LDS;
   * the same kernel with the roles swapped for few output columns over many
     tokens (N <= 128, M >= 2048): 16 tokens per workgroup;
   * split-K: the contraction split into int32 partials that one more launch
@@ -45,7 +45,9 @@ SHAPES = [(1, 4096, 4096), (7, 4096, 4096), (77, 4096, 4096), (128, 4096, 4096),
           # few output columns over many tokens (the roles swapped): tile counts
           # ceil(N / 16) = 1, 3 (LDS), 7 (ragged, LDS) and 8 (LDS); K = 8192 direct
           (2048, 4096, 16), (4096, 2048, 48), (3000, 1024, 100), (2048, 4096, 128),
-          (2500, 8192, 24)]
+          (2500, 8192, 24),
+          # few tokens and few or ragged output columns
+          (1, 4096, 32), (16, 4096, 256), (77, 4096, 1000), (128, 1024, 64)]
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
