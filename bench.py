@@ -199,6 +199,7 @@ def main():
         extra.update(bench_embedding(cr, torch, dev, dev_normal, time_ms, wl))
         extra.update(bench_mlp(cr, torch, dev, dev_normal, time_ms, wl))
         extra.update(bench_packed(cr, torch, dev, dev_normal, time_ms, wl))
+        extra.update(bench_vendor_int8(torch, dev, time_ms, extra.get("gemm_kernel_us")))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -231,6 +232,28 @@ def gemm_traffic():
     except (OSError, ValueError):
         pass
     return None
+
+
+def bench_vendor_int8(torch, dev, time_ms, gemm_us):
+    """Reference only, not part of the layer: the vendor library's int8 GEMM
+    (torch._int_mm through hipBLASLt, int32 output, no epilogue) at 4096^3 and at
+    8192^3, where it runs fastest among the shapes tried.  Its rate is the
+    practical int8 ceiling of the chip under load, beside the datasheet peak."""
+    r = {}
+    for n in (4096, 8192):
+        a = torch.randint(-127, 128, (n, n), dtype=torch.int8, device=dev)
+        b = torch.randint(-127, 128, (n, n), dtype=torch.int8, device=dev)
+        bt = b.t()
+        ms = time_ms(lambda: torch._int_mm(a, bt), 3, 20)
+        r[f"vendor_int8_gemm_{n}_us"] = round(ms * 1e3, 2)
+        r[f"vendor_int8_gemm_{n}_tops"] = round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+        del a, b, bt
+    if gemm_us:
+        ours = 2 * 4096 ** 3 / (gemm_us * 1e-6) / 1e12
+        r["gemm_pct_of_vendor_best_tops"] = round(100 * ours / r["vendor_int8_gemm_8192_tops"], 1)
+    log(f"[bench] vendor int8 GEMM (reference): 4096^3 {r['vendor_int8_gemm_4096_us']} us, "
+        f"8192^3 {r['vendor_int8_gemm_8192_tops']} TOPS")
+    return r
 
 
 def bench_qkv(cr, torch, dev, dev_normal, time_ms, wl):
