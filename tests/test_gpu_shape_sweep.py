@@ -1,0 +1,89 @@
+"""Seeded sweep of layer shapes across every dispatch boundary of the forward and
+both input gradients.
+
+The forward picks among the tiled GEMM, split-K and the few-row kernel (either
+role) from M, N and K; the shapes here are drawn around those boundaries (M near
+128 and 2048, N near 128, 2048 and 8192, K from 128 to 12288, ragged sizes).
+For each shape:
+  * the forward equals the one-pass stages (quantize_act, then the int8 GEMM
+    with its dequantizing epilogue) bit for bit, whichever path it took;
+  * two sampled rows of the forward and of both input gradients match the
+    oracle: exact codes, scales and int32 sums, and outputs within the 1e-2 row
+    tolerance.
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from gpu_util import assert_exact, assert_rows_close, bf16_to_dev, bits, host  # noqa: E402
+
+
+def _shapes():
+    g = np.random.default_rng(20261202)
+    picks = []
+    Ms = [1, 5, 64, 127, 128, 129, 300, 1000, 2047, 2048, 2500, 4096]
+    Ns = [8, 24, 100, 128, 130, 640, 2000, 2048, 4100, 8192, 8200, 12288]
+    Ks = [128, 256, 640, 1024, 2048, 4096, 8192, 12288]
+    for _ in range(28):
+        M, N, K = int(g.choice(Ms)), int(g.choice(Ns)), int(g.choice(Ks))
+        # keep each case to about a second, the oracle's full-weight quantization included
+        while N * K > 1 << 25 or M * N * K > 1 << 35:
+            K = max(128, K // 2)
+            if N * K > 1 << 25 or M * N * K > 1 << 35:
+                N = max(8, N // 2)
+        picks.append((M, N, K))
+    # few output columns over many tokens (the swapped few-row path)
+    picks += [(2048, 100, 1024), (3000, 24, 2048), (4096, 128, 512)]
+    return sorted(set(picks))
+
+
+@pytest.fixture(scope="module")
+def cr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w8a8_rotated_int8_amd as cr
+    cr.lib()
+    return cr
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.lib()
+    return oracle
+
+
+@pytest.mark.parametrize("M,N,K", _shapes())
+def test_shape(cr, orc, M, N, K):
+    print(f"sweep M={M} N={N} K={K}", flush=True)
+    base = M + 7 * N + 13 * K
+    x = wl.activations(M, K, max(1, wl.n_outliers(K)), base=base)
+    w = wl.packed_weight(base % 997, base, N, K)
+    qw, sw = cr.quantize_weight(bf16_to_dev(w))
+    xd = bf16_to_dev(x)
+    y = cr.linear_fwd(xd, qw, sw)
+    qx, sx = cr.quantize_act(xd)
+    assert torch.equal(y, cr.gemm_i8_bf16(qx, sx, qw, sw)), "forward differs from its stages"
+
+    rows = np.unique(np.array([0, M - 1, (M * 5) // 7]))
+    oqw, osw, _ = orc.rotate_quantize(w)
+    assert_exact(host(qw), oqw, "q_w")
+    assert_exact(host(sw), osw, "s_w")
+    oqx, osx, _ = orc.rotate_quantize(x[rows])
+    assert_exact(host(qx)[rows], oqx, "q_x rows")
+    assert_exact(host(sx)[rows], osx, "s_x rows")
+    oacc = orc.gemm_i8_i32(oqx, oqw)
+    assert_rows_close(bits(y)[rows], orc.dequant_epilogue(oacc, osx, osw), "y rows")
+
+    if N % 128 == 0:
+        dy = wl.normal_bf16((M, N), 1e-3, base, 3)
+        dyd = bf16_to_dev(dy)
+        dx8 = cr.linear_bwd_dx(dyd, qw, sw, cr.BWD_INT8)
+        dx16 = cr.linear_bwd_dx(dyd, qw, sw, cr.BWD_BF16)
+        assert_rows_close(bits(dx8)[rows], orc.bwd_dx_int8(dy[rows], oqw, osw)["dx"], "int8 dX rows")
+        assert_rows_close(bits(dx16)[rows], orc.bwd_dx_bf16(dy[rows], oqw, osw)["dx"], "bf16 dX rows")
