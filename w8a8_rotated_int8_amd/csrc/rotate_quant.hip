@@ -45,16 +45,15 @@ __global__ __launch_bounds__(256) void rotate_quant_rows_kernel(
   const int nbk = (rh < rows_per_wave ? (int)rh : rows_per_wave) * nb;
   stage_span<SB, STREAM>(x, r0 * (int64_t)K, nbk, buf);
   uint8_t* cs = lds + 4 * span_bytes<SB>() + wave * SB * 512;  // fold mode: column scales
-  if constexpr (MODE == kFold) stage_colscale<SB>(colscale, nbk, nb, 0, 1, cs);
+  if constexpr (MODE == kFold) stage_colscale<SB>(colscale, nbk, nb, cs);
   wait_vm_n<0>();
-  quantize_span<MODE, SB, MODE == kFold, STREAM>(buf, nbk, nb, r0 * (int64_t)K, 0, r0, 1, q,
-                                                 scale, colscale, seg_max[wave], nullptr, cs);
+  quantize_span<MODE, SB, STREAM>(buf, nbk, nb, r0 * (int64_t)K, r0, 1, q, scale, seg_max[wave],
+                                  nullptr, cs);
 }
 
-// Long rows (K >= 128 * kSpan): one row per workgroup, one SB-block slice per
-// wave; the waves combine their maxima through LDS.  CSL (fold mode): the
-// column scales of each slice are staged in LDS past the rows' slices.
-template <int MODE, int SB, bool CSL, bool STREAM>
+// Long rows (K >= 128 * kSpan), rotate mode: one row per workgroup, one
+// SB-block slice per wave; the waves combine their maxima through LDS.
+template <int MODE, int SB, bool STREAM>
 __global__ __launch_bounds__(SB == 16 ? 1024 : 512) void rotate_quant_long_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int K, int8_t* __restrict__ q,
     float* __restrict__ scale, const float* __restrict__ colscale, int waves_per_row) {
@@ -69,13 +68,81 @@ __global__ __launch_bounds__(SB == 16 ? 1024 : 512) void rotate_quant_long_kerne
   const int64_t span_elem0 = row0 * (int64_t)K + (int64_t)blk_in_row0 * kBlock;
   uint8_t* my_lds = lds + wave * span_bytes<SB>();
   stage_span<SB, STREAM>(x, span_elem0, span_blocks, my_lds);
-  uint8_t* cs = lds + waves_per_row * span_bytes<SB>() + wave * SB * 512;
-  if constexpr (CSL)
-    stage_colscale<SB>(colscale, span_blocks, nb, blk_in_row0, waves_per_row, cs);
   wait_vm_n<0>();
-  quantize_span<MODE, SB, CSL, STREAM>(my_lds, span_blocks, nb, span_elem0, blk_in_row0, row0,
-                                       waves_per_row, q, scale, colscale, nullptr, row_part_max,
-                                       cs);
+  quantize_span<MODE, SB, STREAM>(my_lds, span_blocks, nb, span_elem0, row0,
+                                  waves_per_row, q, scale, nullptr, row_part_max);
+}
+
+// Fold mode, rows of at least one span (N >= 128 * kSpan): one row per
+// workgroup and no LDS staging.  Folding has no data flow between elements, so
+// lane t of the workgroup takes the 4-element units t + j * blockDim.x
+// (j < kFoldUnits): the row's bf16 loads, the column-scale loads and the code
+// stores are each contiguous across a wave's lanes.  The waves combine their
+// maxima through LDS.  The arithmetic per element and per row is that of the
+// span quantizer's fold mode: r = fl32(dY) * s_w, a = max |r|, s = fl32(a/127),
+// code = RNE(fl32(r/s)).
+constexpr int kFoldUnits = 8;
+
+__global__ __launch_bounds__(1024) void fold_quant_rows_kernel(
+    const uint16_t* __restrict__ dy, int N, int8_t* __restrict__ q, float* __restrict__ scale,
+    const float* __restrict__ colscale) {
+  __shared__ float part[16];
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int lane = tid & 63, wave = tid >> 6, nwaves = nthr >> 6;
+  const int units = N >> 2;
+  const int64_t row = blockIdx.x;
+  const uint2* src = reinterpret_cast<const uint2*>(dy + row * (int64_t)N);
+  const float4* cs = reinterpret_cast<const float4*>(colscale);
+  uint2 raw[kFoldUnits];
+  float4 sc[kFoldUnits];
+#pragma unroll
+  for (int j = 0; j < kFoldUnits; ++j) {
+    const int u = j * nthr + tid;
+    raw[j] = u < units ? src[u] : make_uint2(0u, 0u);
+    sc[j] = u < units ? cs[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float r[kFoldUnits][4];
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < kFoldUnits; ++j) {
+    r[j][0] = bf16lo_to_f32(raw[j].x) * sc[j].x;
+    r[j][1] = bf16hi_to_f32(raw[j].x) * sc[j].y;
+    r[j][2] = bf16lo_to_f32(raw[j].y) * sc[j].z;
+    r[j][3] = bf16hi_to_f32(raw[j].y) * sc[j].w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(r[j][e]));
+  }
+  m = max_xor32(max_xor16(group_max(m, 16)));
+  if (lane == 0) part[wave] = m;
+  __syncthreads();
+  m = 0.f;
+  for (int w = 0; w < nwaves; ++w) m = fmaxf(m, part[w]);
+
+  // m is the same in every lane, so both branches are workgroup-uniform.
+  float s, t[kFoldUnits][4];
+  if (m >= 0x1p-64f && m <= 0x1p100f) {
+    s = quot_rn(m, 127.0f, kInv127);
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int j = 0; j < kFoldUnits; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[j][e] = quot_rn(r[j][e], s, inv);
+  } else {
+    s = m / 127.0f;
+#pragma unroll
+    for (int j = 0; j < kFoldUnits; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[j][e] = s > 0.f ? r[j][e] / s : 0.f;
+  }
+  uint32_t* dst = reinterpret_cast<uint32_t*>(q + row * (int64_t)N);
+#pragma unroll
+  for (int j = 0; j < kFoldUnits; ++j) {
+    const int u = j * nthr + tid;
+    if (u < units)
+      dst[u] = pack_low_bytes(rne_low_byte_bits(t[j][0]), rne_low_byte_bits(t[j][1]),
+                              rne_low_byte_bits(t[j][2]), rne_low_byte_bits(t[j][3]));
+  }
+  if (tid == 0) scale[row] = s;
 }
 
 }  // namespace
@@ -102,22 +169,13 @@ hipError_t launch_rotate_quant(const uint16_t* x, int64_t rows, int K, int8_t* q
   if (rows <= 0) return hipSuccess;
   if (fold && weights) return hipErrorInvalidValue;
   RowPlan pl = plan_rows(K);
-  // Fold-mode column scales staged in LDS cost 8 KB per wave beside its 4 KB
-  // span.  They are staged when a CU still holds at least 12 waves of the
-  // kernel that way (3 per SIMD; measured: 8 slices per row, one workgroup of 8
-  // waves per CU, ran 5% slower than reading the scales from global memory).
-  constexpr int kMaxCslWaves = 12;
-  constexpr int kLdsPerCu = 160 * 1024;
   {
     static std::atomic<uint64_t> configured{0};
     const int max_lds = CONVROT_MAX_ROW_LEN_BLOCKS * 256;
-    const void* ks[4] = {(const void*)rotate_quant_long_kernel<kRotate, kSpan, false, false>,
-                         (const void*)rotate_quant_long_kernel<kRotate, kSpan, false, true>,
-                         (const void*)rotate_quant_long_kernel<kFold, kSpan, false, false>,
-                         (const void*)rotate_quant_long_kernel<kFold, kSpan, true, false>};
-    const int lim[4] = {max_lds, max_lds, max_lds,
-                        kMaxCslWaves * (span_bytes<kSpan>() + kSpan * 512)};
-    hipError_t e = set_lds_limits_once(ks, lim, 4, configured);
+    const void* ks[2] = {(const void*)rotate_quant_long_kernel<kRotate, kSpan, false>,
+                         (const void*)rotate_quant_long_kernel<kRotate, kSpan, true>};
+    const int lim[2] = {max_lds, max_lds};
+    hipError_t e = set_lds_limits_once(ks, lim, 2, configured);
     if (e != hipSuccess) return e;
   }
   if (K / kBlock < kSpan) {
@@ -136,26 +194,21 @@ hipError_t launch_rotate_quant(const uint16_t* x, int64_t rows, int K, int8_t* q
       hipLaunchKernelGGL((rotate_quant_rows_kernel<kRotate, kSpan, false>), dim3((unsigned)grid),
                          dim3(256), 4 * span_bytes<kSpan>(), stream, x, rows, K, q, scale, colscale,
                          pl.rows_per_wave);
+  } else if (fold) {
+    if (rows > 0x7fffffff) return hipErrorInvalidValue;
+    const int units = K / 4;
+    const int waves = (units + 64 * kFoldUnits - 1) / (64 * kFoldUnits);  // <= 16 for K <= 32768
+    hipLaunchKernelGGL(fold_quant_rows_kernel, dim3((unsigned)rows), dim3(64 * waves), 0, stream,
+                       x, K, q, scale, colscale);
   } else {
     if (rows > 0x7fffffff) return hipErrorInvalidValue;
     const size_t lds = (size_t)pl.waves_per_row * span_bytes<kSpan>();
-    const int csl_wg = pl.waves_per_row * (span_bytes<kSpan>() + kSpan * 512);
-    const bool csl = pl.waves_per_row <= kMaxCslWaves &&
-                     (kLdsPerCu / csl_wg) * pl.waves_per_row >= 12;
-    if (fold && csl)
-      hipLaunchKernelGGL((rotate_quant_long_kernel<kFold, kSpan, true, false>), dim3((unsigned)rows),
-                         dim3(pl.threads), lds + (size_t)pl.waves_per_row * kSpan * 512, stream, x,
-                         rows, K, q, scale, colscale, pl.waves_per_row);
-    else if (fold)
-      hipLaunchKernelGGL((rotate_quant_long_kernel<kFold, kSpan, false, false>), dim3((unsigned)rows),
-                         dim3(pl.threads), lds, stream, x, rows, K, q, scale, colscale,
-                         pl.waves_per_row);
-    else if (weights)
-      hipLaunchKernelGGL((rotate_quant_long_kernel<kRotate, kSpan, false, true>), dim3((unsigned)rows),
+    if (weights)
+      hipLaunchKernelGGL((rotate_quant_long_kernel<kRotate, kSpan, true>), dim3((unsigned)rows),
                          dim3(pl.threads), lds, stream, x, rows, K, q, scale, colscale,
                          pl.waves_per_row);
     else
-      hipLaunchKernelGGL((rotate_quant_long_kernel<kRotate, kSpan, false, false>),
+      hipLaunchKernelGGL((rotate_quant_long_kernel<kRotate, kSpan, false>),
                          dim3((unsigned)rows), dim3(pl.threads), lds, stream, x, rows, K, q, scale,
                          colscale, pl.waves_per_row);
   }

@@ -22,6 +22,9 @@
 // with L + 16 (v_permlane16_swap) and the seventh with L + 32
 // (v_permlane32_swap).  A 16-block span keeps 32 values per lane and fits in
 // ~100 VGPRs (four waves per SIMD); a 32-block span keeps 64 (~150 VGPRs).
+// Fold mode comes here only for packed short rows, with the column scales
+// staged in LDS beside the span; rows of a span or longer are folded by a
+// kernel of their own that needs no transposed layout.
 #pragma once
 
 #include "common.h"
@@ -63,12 +66,11 @@ __device__ __forceinline__ void swap_rows16(double& vdst, double& src0) {
 // register bit 4 with a lane bit, so that the butterfly partners meet in one
 // lane.  After both, lane quarter q = L >> 4 holds outputs 16 q + e in v[e]
 // and 64 + 16 q + e in v[e + 16] (e < 16).
-template <int MODE, int SB = kSpanBlocks, bool CSL = false, bool STREAM = false>
+template <int MODE, int SB = kSpanBlocks, bool STREAM = false>
 __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_blocks, int nb,
-                                              int64_t span_elem0, int blk_in_row0, int64_t row0,
+                                              int64_t span_elem0, int64_t row0,
                                               int waves_per_row, int8_t* __restrict__ q,
                                               float* __restrict__ scale,
-                                              const float* __restrict__ colscale,
                                               float* seg_max_wave, float* row_part_max,
                                               const uint8_t* cs_lds = nullptr) {
 #pragma clang fp contract(off)
@@ -141,18 +143,11 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
 #pragma unroll
       for (int e = 0; e < 32; ++e) r[k][e] = (float)(v[e] * kInvSqrt128);
     } else {
-      // fold the per-column scale: element 32 g + e of block b.  With CSL the
-      // span's scales were staged at cs_lds by stage_colscale (chunk c of block b
-      // at b * 32 + (c ^ (b & 15))); otherwise they are read from global memory.
-      const int64_t col0 =
-          active ? (int64_t)(blk_in_row0 + (waves_per_row == 1 ? b % nb : b)) * kBlock + 32 * g
-                 : 0;
-      const float4* cs = reinterpret_cast<const float4*>(colscale + col0);
+      // fold the per-column scale: element 32 g + e of block b.  The span's
+      // scales were staged at cs_lds by stage_colscale (chunk c of block b at
+      // b * 32 + (c ^ (b & 15))).
       auto scale4 = [&](int i2) {  // floats 32 g + 4 i2 .. + 3 of block b
-        if constexpr (CSL)
-          return *reinterpret_cast<const float4*>(cs_lds + b * 512 + 16 * ((8 * g + i2) ^ (b & 15)));
-        else
-          return active ? cs[i2] : make_float4(0.f, 0.f, 0.f, 0.f);
+        return *reinterpret_cast<const float4*>(cs_lds + b * 512 + 16 * ((8 * g + i2) ^ (b & 15)));
       };
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -302,16 +297,16 @@ __device__ __forceinline__ void stage_span(const uint16_t* __restrict__ x, int64
   }
 }
 
-// Fold mode: copy the per-column scales of a span's blocks (128 floats, 32
-// chunks of 16 bytes per block) to LDS with coalesced direct loads, SB / 2 per
+// Fold mode, short rows packed into a span (block b of the span is block
+// b % nb of its row): copy the per-column scales of the span's blocks (128
+// floats, 32 chunks of 16 bytes per block) to LDS with coalesced direct loads, SB / 2 per
 // lane.  Chunk c of span block b lands at b * 32 + (c ^ (b & 15)): the fold
 // pass reads chunk 8 g + i of block p in lanes 16 g + p, and the XOR spreads
 // those 16 lanes over 16 different bank groups.  Blocks past the span reload
 // a chunk of its last block (never read).
 template <int SB>
 __device__ __forceinline__ void stage_colscale(const float* __restrict__ colscale, int span_blocks,
-                                               int nb, int blk_in_row0, int waves_per_row,
-                                               uint8_t* cs_lds) {
+                                               int nb, uint8_t* cs_lds) {
   const int lane = threadIdx.x & 63;
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_u32(cs_lds));
 #pragma unroll
@@ -320,8 +315,7 @@ __device__ __forceinline__ void stage_colscale(const float* __restrict__ colscal
     int b = slot >> 5;
     int c = (slot & 31) ^ (b & 15);
     if (b >= span_blocks) { b = span_blocks - 1; c = 0; }
-    const int gb = blk_in_row0 + (waves_per_row == 1 ? b % nb : b);
-    dma16(colscale + (int64_t)gb * kBlock + 4 * c, base + i * 1024);
+    dma16(colscale + (int64_t)(b % nb) * kBlock + 4 * c, base + i * 1024);
   }
 }
 
