@@ -210,14 +210,28 @@ def test_linear_fwd_attn_full_size(cr, orc):
 @pytest.mark.parametrize("M,N", [(33, 256), (17, 1152), (9, 2048), (7, 4224), (5, 16384),
                                  (3, 24576), (3, 24704), (2, 32768)])
 def test_bwd_quant_dy_exact(cr, orc, M, N):
-    # the dY quantizer on every row plan: packed short rows, slices with the
-    # column scales staged in LDS (up to 12 slices), and longer rows that read
-    # them from global memory
+    # the dY quantizer on both row plans: short rows packed into a span with the
+    # column scales staged beside it, and rows of 2048 values or more folded one
+    # row per workgroup (1, 2, 3, 8, 12, 13 and 16 waves)
     say(f"bwd_quant_dy M={M} N={N}")
     dy = wl.normal_bf16((M, N), 1e-3, 11, N % 1000)
     sw = (np.random.default_rng(N).random(N) * 1e-3 + 1e-5).astype(np.float32)
     qg, sg = cr.bwd_quant_dy(bf16_to_dev(dy), torch.from_numpy(sw).cuda())
     oqg, osg = orc.bwd_quant_dy(dy, sw)
+    assert_exact(host(sg), osg, "s_g")
+    assert_exact(host(qg), oqg, "q_g")
+
+
+@pytest.mark.parametrize("N", [256, 1152, 2048, 4224, 32768])
+def test_bwd_quant_dy_crafted_rows(cr, orc, N):
+    # the quantizer's corner rows (all zero, exact ties, IEEE-division scales)
+    # through the fold; power-of-two column scales keep the folded ties exact
+    say(f"bwd_quant_dy crafted rows N={N}")
+    dy = crafted_rows(N)
+    sw = np.ldexp(np.ones(N, np.float32), -(np.arange(N) % 7)).astype(np.float32)
+    qg, sg = cr.bwd_quant_dy(bf16_to_dev(dy), torch.from_numpy(sw).cuda())
+    oqg, osg = orc.bwd_quant_dy(dy, sw)
+    assert osg[0] == 0 and not oqg[0].any()
     assert_exact(host(sg), osg, "s_g")
     assert_exact(host(qg), oqg, "q_g")
 
