@@ -4,7 +4,7 @@ Every entry point is stream-ordered and allocates nothing, so a caller may
 capture it (bench.py times the few-row forwards that way).  Each graph is
 replayed several times with eager work on the same buffers in between, and every
 replay must reproduce the eager result bit for bit: one case per forward path
-(few-row kernel, split-K, tiled GEMM) and the int8 backward.
+(few-row kernel, its split form, split-K, tiled GEMM) and the int8 backward.
 """
 import pytest
 
@@ -39,7 +39,8 @@ def capture(fn):
     return g
 
 
-@pytest.mark.parametrize("M,K,N", [(77, 4096, 4096), (300, 4096, 4096), (4096, 512, 2048)])
+@pytest.mark.parametrize("M,K,N", [(77, 4096, 4096), (100, 8192, 1000), (300, 4096, 4096),
+                                   (4096, 512, 2048)])
 def test_forward_graph_replays(cr, M, K, N):
     print(f"graph forward M={M} K={K} N={N}", flush=True)
     x = bf16_to_dev(wl.activations(M, K, wl.n_outliers(K), base=5))

@@ -3,7 +3,9 @@ outputs (N = 32), as in the training guide's text-encoder quantization
 (section 7.1, text encoder bullet).  With few 256 x 256 output tiles the
 forward runs one of three paths:
   * the few-row kernel (M <= 128, N <= 8192, K <= 8192): 16 output columns per
-    workgroup, the waves' int32 sums added in LDS;
+    workgroup, the waves' int32 sums added in LDS; for K = 8192 and more than 32
+    rows its split form, 64 columns and a 1 KB K-slice per workgroup into int32
+    partials that one more launch sums and dequantizes;
   * the same kernel with the roles swapped for few output columns over many
     tokens (N <= 128, M >= 2048): 16 tokens per workgroup;
   * split-K: the contraction split into int32 partials that one more launch
@@ -47,7 +49,10 @@ SHAPES = [(1, 4096, 4096), (7, 4096, 4096), (77, 4096, 4096), (128, 4096, 4096),
           (2048, 4096, 16), (4096, 2048, 48), (3000, 1024, 100), (2048, 4096, 128),
           (2500, 8192, 24),
           # few tokens and few or ragged output columns
-          (1, 4096, 32), (16, 4096, 256), (77, 4096, 1000), (128, 1024, 64)]
+          (1, 4096, 32), (16, 4096, 256), (77, 4096, 1000), (128, 1024, 64),
+          # the split few-row form (K = 8192, 3 to 8 row tiles, ragged column groups)
+          (33, 8192, 4096), (128, 8192, 8192), (100, 8192, 1000), (50, 8192, 4092),
+          (32, 8192, 1024)]
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
@@ -76,7 +81,8 @@ def test_small_m_forward(cr, M, K, N):
     print(f"  max row relerr {e:.2e}", flush=True)
 
 
-@pytest.mark.parametrize("M,K,N", [(77, 4096, 4096), (4096, 4096, 32), (2048, 2048, 100)])
+@pytest.mark.parametrize("M,K,N", [(77, 4096, 4096), (4096, 4096, 32), (2048, 2048, 100),
+                                   (77, 8192, 2048)])
 def test_small_m_with_bias(cr, M, K, N):
     x = wl.activations(M, K, wl.n_outliers(K), base=1)
     w = wl.packed_weight(4100, 1, N, K)

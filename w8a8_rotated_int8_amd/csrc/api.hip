@@ -63,7 +63,7 @@ size_t fwd_workspace(int64_t M, int64_t K) { return align256((size_t)M * K) + al
 // The forward also holds the int32 partials of a split-K GEMM when the shape
 // has too few output tiles to fill the chip (small M, or skinny N).
 size_t fwd_splitk_workspace(int64_t M, int64_t N, int64_t K) {
-  const int S = splitk_factor(M, N, K);
+  const int S = small_m_mode(M, N, K) ? small_m_split(M, N, K) : splitk_factor(M, N, K);
   return S > 1 ? align256((size_t)S * M * N * 4) : 0;
 }
 size_t bwd_int8_workspace(int64_t M, int64_t N) {
@@ -150,16 +150,14 @@ int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw
   float* sx = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + align256((size_t)M * K));
   hipError_t e = launch_rotate_quant(x, M, (int)K, qx, sx, nullptr, false, false, stream);
   if (e != hipSuccess) return CONVROT_EHIP;
+  int32_t* partial = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + fwd_workspace(M, K));
   if (small_m_mode(M, N, K))
-    return hip_status(launch_gemm_small_m(qx, sx, qw, sw, bias, M, N, K, y, stream));
+    return hip_status(launch_gemm_small_m(qx, sx, qw, sw, bias, M, N, K, y, partial, stream));
   GemmArgs a{};
   a.P = qw; a.Q = qx; a.I = N; a.J = M; a.Kc = K; a.ldp = K; a.ldq = K;
   a.out = y; a.ldo = N; a.si = sw; a.sj = sx; a.bias = bias;
   const int S = splitk_factor(M, N, K);
-  if (S > 1) {
-    int32_t* partial = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + fwd_workspace(M, K));
-    return hip_status(launch_gemm_i8_splitk_dequant(a, S, partial, stream));
-  }
+  if (S > 1) return hip_status(launch_gemm_i8_splitk_dequant(a, S, partial, stream));
   return hip_status(launch_gemm_i8(a, kEpiDequantBf16, false, stream));
 }
 

@@ -704,11 +704,20 @@ hipError_t launch_gemm_i8_splitk_dequant(const GemmArgs& a, int S, int32_t* part
                      a.Kc / S, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t quads = a.J * (a.I / 4);
+  return launch_splitk_dequant(partial, S, a.J, a.I, a.si, a.sj, a.bias,
+                               static_cast<uint16_t*>(a.out), stream);
+}
+
+hipError_t launch_splitk_dequant(const int32_t* partial, int S, int64_t J, int64_t I,
+                                 const float* si, const float* sj, const uint16_t* bias,
+                                 uint16_t* out, hipStream_t stream) {
+  if (S < 1 || I % 4) return hipErrorInvalidValue;
+  const int64_t quads = J * (I / 4);
   const int64_t blocks = (quads + 255) / 256;
+  if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(splitk_dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, partial, S,
-                     a.J, a.I, a.si, a.sj, a.bias, static_cast<uint16_t*>(a.out));
+                     J, I, si, sj, bias, out);
   return hipGetLastError();
 }
 

@@ -207,6 +207,112 @@ __global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_lds_kernel(
   }
 }
 
+// Split-K form, for three or more row tiles.  The one-pass kernels above read
+// all of q_x in every workgroup (16 output columns each), and those re-reads
+// from L2 bound them.  Here workgroup (x, y) owns the kSmCols 16-column tiles
+// from 16 kSmCols x and the K-slice [kSmSlice y, kSmSlice (y + 1)): four times
+// the columns per q_x byte read, with the K split restoring the workgroup
+// count.  The q_w steps of both 512-byte chunks of the slice are loaded first,
+// then both chunks of q_x are staged at once in the swizzled layout of
+// gemm_small_m_lds_kernel; wave w multiplies step w of each chunk against its
+// column tiles, the waves add their tiles in LDS with integer atomics, and the
+// int32 sums go to partial[y][m][n].  The dequantizing launch after it adds
+// the slices (exact) and applies the fp32 epilogue in store_out's order, so
+// the output is bit-identical to the one-pass kernels'.
+constexpr int kSmCols = 4;
+constexpr int kSmSlice = 2 * kSmChunk;
+
+template <int T>
+__global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_splitk_kernel(
+    const int8_t* __restrict__ qx, const int8_t* __restrict__ qw, int64_t M, int64_t N,
+    int64_t K, int32_t* __restrict__ partial) {
+  extern __shared__ __align__(16) uint8_t xs[];  // 2 chunks of 16 T rows x 512 bytes
+  __shared__ int32_t part[T][kSmCols][4][64];
+  for (int i = threadIdx.x; i < T * kSmCols * 256; i += 64 * kSmWaves) (&part[0][0][0][0])[i] = 0;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * kSmCols;
+  const int64_t k0 = (int64_t)blockIdx.y * kSmSlice;
+  uint4 wv[2][kSmCols];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int j = 0; j < kSmCols; ++j) {
+      const int64_t n = n0 + 16 * j + r < N ? n0 + 16 * j + r : N - 1;  // past the end: reload
+      wv[c][j] = *reinterpret_cast<const uint4*>(qw + n * K + k0 + c * kSmChunk + 64 * wave + 16 * g);
+    }
+  __builtin_amdgcn_sched_barrier(0);  // the q_w loads ahead of the direct loads
+  constexpr int kBuf = 16 * T * kSmChunk;
+  const uint32_t xs_base = __builtin_amdgcn_readfirstlane(lds_u32(xs));
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int it = 0; it < T; ++it) {
+      const int inst = it * kSmWaves + wave;  // 1 KB piece of the chunk
+      const int slot = inst * 64 + lane;
+      const int row = slot >> 5;
+      const int pc = (slot & 31) ^ (row & 15);  // the 16-byte piece this lane fetches
+      const int64_t m = row < M ? row : M - 1;  // rows past the end reload the last one
+      dma16(qx + m * K + k0 + c * kSmChunk + 16 * pc, xs_base + c * kBuf + inst * 1024);
+    }
+  wait_vm_n<0>();
+  __syncthreads();  // every wave's pieces landed; part is zeroed
+  v4i acc[T][kSmCols];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int j = 0; j < kSmCols; ++j) acc[t][j] = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int row = 16 * t + r;
+      const uint4 xf = *reinterpret_cast<const uint4*>(xs + c * kBuf + row * kSmChunk +
+                                                       16 * ((4 * wave + g) ^ r));
+#pragma unroll
+      for (int j = 0; j < kSmCols; ++j)
+        acc[t][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xf),
+                                                          __builtin_bit_cast(v4i, wv[c][j]),
+                                                          acc[t][j], 0, 0, 0);
+    }
+  // lane l holds rows 4 (l / 16) + v of row tile t, column l % 16 of column tile j
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int j = 0; j < kSmCols; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) atomicAdd(&part[t][j][v][lane], acc[t][j][v]);
+  __syncthreads();
+  int32_t* out = partial + (int64_t)blockIdx.y * M * N;
+  for (int idx = threadIdx.x; idx < T * kSmCols * 256; idx += 64 * kSmWaves) {
+    const int l = idx & 63, v = (idx >> 6) & 3, j = (idx >> 8) & (kSmCols - 1), t = idx >> 10;
+    const int64_t m = 16 * t + 4 * (l >> 4) + v;
+    const int64_t nn = n0 + 16 * j + (l & 15);
+    if (m < M && nn < N) out[m * N + nn] = part[t][j][v][l];
+  }
+}
+
+template <int T>
+hipError_t launch_split_t(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw,
+                          const uint16_t* bias, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                          int32_t* partial, hipStream_t stream) {
+  static_assert(kSmCols == 4, "the partial store decodes the column tile with a 2-bit mask");
+  constexpr int kLds = 2 * 16 * T * kSmChunk;  // + T KB x kSmCols of static int32 sums
+  static_assert(kLds + T * kSmCols * 1024 <= 160 * 1024, "fits the 160 KB of LDS");
+  static std::atomic<uint64_t> configured{0};
+  const void* k = (const void*)gemm_small_m_splitk_kernel<T>;
+  hipError_t e = set_lds_limits_once(&k, &kLds, 1, configured);
+  if (e != hipSuccess) return e;
+  const int64_t gx = (N + 16 * kSmCols - 1) / (16 * kSmCols);
+  const int64_t S = K / kSmSlice;
+  hipLaunchKernelGGL((gemm_small_m_splitk_kernel<T>), dim3((unsigned)gx, (unsigned)S),
+                     dim3(64 * kSmWaves), kLds, stream, qx, qw, M, N, K, partial);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_splitk_dequant(partial, (int)S, M, N, sw, sx, bias, y, stream);
+}
+
 // In kernel terms: M few rows (qx, sx), N many (qw, sw); SW when the few are
 // the weight's rows (see store_out).
 template <int T, bool SW>
@@ -254,6 +360,19 @@ hipError_t launch_few(const int8_t* qx, const float* sx, const int8_t* qw, const
 
 }  // namespace
 
+// The split form for few rows: three or more row tiles, K beyond what the
+// staged one-pass kernel holds (K > 4096, whole 1 KB slices) and N % 4 == 0 for
+// the dequantizing launch.  Measured (forward, graph replays, same box):
+// 128 x 8192 x 8192 73.6 -> 51.6 us, 100 x 8192 x 1000 33.7 -> 18.2 us,
+// 77 x 8192 x 4096 28.2 -> 25.8 us; at K = 4096 the pipelined one-pass kernel
+// stays faster (77 x 4096 x 4096 13.0 against 16.0 us split), and taking
+// K >= 12288 into this form lost to the tiled split-K (77 x 16384 x 4096 33.4
+// against 44.5 us).
+static bool small_m_split_fits(int64_t M, int64_t N, int64_t K) {
+  return M > 32 && M <= kSmallM && N >= 1 && N % 4 == 0 && K % kSmSlice == 0 &&
+         K > (int64_t)kSmChunk * kSmMaxChunks && K <= (int64_t)CONVROT_MAX_ROW_LEN_BLOCKS * kBlock;
+}
+
 int small_m_mode(int64_t M, int64_t N, int64_t K) {
   if (K % 64 || K > 8192) return 0;
   // Measured against split-K (forward, M = 1..128, K = 4096): faster for every
@@ -267,11 +386,27 @@ int small_m_mode(int64_t M, int64_t N, int64_t K) {
   return 0;
 }
 
+int small_m_split(int64_t M, int64_t N, int64_t K) {
+  if (small_m_mode(M, N, K) != 1 || !small_m_split_fits(M, N, K)) return 1;
+  return (int)(K / kSmSlice);
+}
+
 hipError_t launch_gemm_small_m(const int8_t* qx, const float* sx, const int8_t* qw,
                                const float* sw, const uint16_t* bias, int64_t M, int64_t N,
-                               int64_t K, uint16_t* y, hipStream_t stream) {
+                               int64_t K, uint16_t* y, int32_t* partial, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
   const int mode = small_m_mode(M, N, K);
+  if (mode == 1 && small_m_split(M, N, K) > 1) {
+    if (!partial) return hipErrorInvalidValue;
+    switch ((M + 15) / 16) {
+      case 3: return launch_split_t<3>(qx, sx, qw, sw, bias, M, N, K, y, partial, stream);
+      case 4: return launch_split_t<4>(qx, sx, qw, sw, bias, M, N, K, y, partial, stream);
+      case 5: return launch_split_t<5>(qx, sx, qw, sw, bias, M, N, K, y, partial, stream);
+      case 6: return launch_split_t<6>(qx, sx, qw, sw, bias, M, N, K, y, partial, stream);
+      case 7: return launch_split_t<7>(qx, sx, qw, sw, bias, M, N, K, y, partial, stream);
+      default: return launch_split_t<8>(qx, sx, qw, sw, bias, M, N, K, y, partial, stream);
+    }
+  }
   if (mode == 1) return launch_few<false>(qx, sx, qw, sw, bias, M, N, K, y, stream);
   if (mode == 2) return launch_few<true>(qw, sw, qx, sx, bias, N, M, K, y, stream);
   return hipErrorInvalidValue;

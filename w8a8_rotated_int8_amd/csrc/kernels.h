@@ -67,9 +67,17 @@ int splitk_factor(int64_t M, int64_t N, int64_t K);
 // small_m_mode says when the forward takes it (0: it does not).
 constexpr int64_t kSmallM = 128;
 int small_m_mode(int64_t M, int64_t N, int64_t K);
+// K-slices of the few-row forward's split form (1: one pass); when above 1 the
+// forward passes int32 partials [S, M, N] (caller-provided workspace).
+int small_m_split(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_small_m(const int8_t* qx, const float* sx, const int8_t* qw,
                                const float* sw, const uint16_t* bias, int64_t M, int64_t N,
-                               int64_t K, uint16_t* y, hipStream_t stream);
+                               int64_t K, uint16_t* y, int32_t* partial, hipStream_t stream);
+// Sum S int32 partials [S, J, I] and dequantize to out[j][i] with the forward
+// epilogue (s_j[j], then s_i[i], then bias[i]).  Needs I % 4 == 0.
+hipError_t launch_splitk_dequant(const int32_t* partial, int S, int64_t J, int64_t I,
+                                 const float* si, const float* sj, const uint16_t* bias,
+                                 uint16_t* out, hipStream_t stream);
 
 // bf16 operands (MFMA f32 32x32x16), both row-major, kEpiBf16.
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t stream);
