@@ -97,10 +97,11 @@ int convrot_quantize_weight(const uint16_t* w, int64_t rows, int64_t cols, int32
  *   y     bf16 [M, N] out
  *   workspace  >= convrot_workspace_bytes(CONVROT_OP_LINEAR_FWD, M, N, K, 0) bytes
  *              of device memory, 256-byte aligned: q_x and s_x, plus int32 partial
- *              sums when few 256 x 256 output tiles make the contraction split
- *              along K.  Which kernels run depends on M, N and K (one tiled GEMM,
- *              a few-row kernel for M <= 128 or for N <= 128, or split-K); y is
- *              the same bit for bit on every path.
+ *              sums when the contraction is split along K (few 256 x 256 output
+ *              tiles, or more than 32 rows at K = 8192 on the few-row path).
+ *              Which kernels run depends on M, N and K (one tiled GEMM, a
+ *              few-row kernel for M <= 128 or for N <= 128, or a split along K);
+ *              y is the same bit for bit on every path.
  */
 int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw,
                        const float* sw, int64_t N, const uint16_t* bias, uint16_t* y,
