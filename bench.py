@@ -14,10 +14,18 @@ The same line carries
     peak; ``traffic`` comes from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     counters when they were taken on the current kernel source, else null;
   * ``cpu_baseline``: the CPU oracle (plain C, OpenMP) on the full forward of
-    the same workload on this host;
+    the same workload on this host, and ``cpu_baselines``: the oracle on the
+    other workloads (tiny layer in full on all threads and on one; bounded row
+    samples of the MLP pair, of one packed-stream layer extrapolated to the
+    252-layer pass, and of the embedding's quantizer and lookup);
   * ``extra``: the other hot-path kernels on their workloads (load-time and
-    embedding quantizers, lookup, both input-gradient modes, the MLP pair and
-    the 252-linear packed stream).
+    embedding quantizers, lookup, both input-gradient modes, the MLP pair, the
+    252-linear packed stream and the text encoder's quantization pass).
+
+HBM figures: the embedding quantizer moves 3 GB per call, far beyond the
+256 MB last-level cache.  The lookup (~0.4 GB per call) is timed call by call
+with a 1 GiB device fill between calls, over four different id sets, so its
+code rows come from HBM; its back-to-back rate is reported beside it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|all]
 """
@@ -58,6 +66,20 @@ def parse():
     return ap.parse_args()
 
 
+def warm_up(torch, fn, min_calls, min_s=0.1):
+    """At least `min_calls` calls and at least `min_s` seconds of back-to-back
+    calls (batches of calls, one synchronization each): the clocks ramp over the
+    first ~35 ms of continuous work, so every timing starts from ramped clocks."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < min_calls or time.perf_counter() - t0 < min_s:
+        for _ in range(max(1, min(min_calls, 16))):
+            fn()
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -89,16 +111,8 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
     def time_ms(fn, warmup, iters, min_warm_s=0.08):
-        # at least `warmup` calls and at least min_warm_s of back-to-back calls
-        # (batches of calls with one synchronization each), so that every
-        # measurement starts from ramped clocks even after host-side setup
-        t0 = time.perf_counter()
-        n = 0
-        while n < warmup or time.perf_counter() - t0 < min_warm_s:
-            for _ in range(max(1, min(warmup, 16))):
-                fn()
-                n += 1
-            torch.cuda.synchronize()
+        # warmed up to ramped clocks even after host-side setup
+        warm_up(torch, fn, warmup, min_warm_s)
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         s.record()
@@ -134,10 +148,9 @@ def main():
     def step():
         cr.linear_fwd(x, qw, sw, out=y, workspace=ws)
 
-    log(f"[bench] headline: {args.warmup} warmup + {args.steps} timed linear_fwd calls")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    nw = warm_up(torch, step, args.warmup, 0.1)
+    log(f"[bench] headline: {nw} warmup calls (>= {args.warmup} and >= 100 ms) + {args.steps} "
+        f"timed linear_fwd calls")
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -164,8 +177,9 @@ def main():
         f"{aq_ms * 1e3:.1f} us ({aq_bytes / (aq_ms * 1e-3) / 1e9:.0f} GB/s, MALL-resident)")
 
     roofline = {
-        "bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
-        "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": gemm_traffic(),
+        "bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
+        "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+        "traffic": counter_traffic("gemm_i8_attn_4096_pmc.json", ["gemm.hip", "common.h"]),
         "kernel": "gemm_kernel<dequant-bf16> (int8 MFMA 32x32x32)", "avg_launch_us": round(gemm_ms * 1e3, 2),
         "algorithmic_ops_per_launch": ops,
     }
@@ -199,11 +213,14 @@ def main():
         extra.update(bench_embedding(cr, torch, dev, dev_normal, time_ms, wl))
         extra.update(bench_mlp(cr, torch, dev, dev_normal, time_ms, wl))
         extra.update(bench_packed(cr, torch, dev, dev_normal, time_ms, wl))
+        extra.update(bench_text_encoder_quant(cr, torch, dev, dev_normal, wl))
         extra.update(bench_vendor_int8(torch, dev, time_ms, extra.get("gemm_kernel_us")))
 
-    cpu = None
+    cpu = cpu_lines = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(a)
+        if args.only == "all":
+            cpu_lines = cpu_baselines(wl)
 
     out = {
         "metric": METRIC, "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1,
@@ -214,20 +231,27 @@ def main():
                                "outlier channels x50, W bf16 [4096, 4096] ~N(0,0.02), block 128; "
                                "fused forward, weight pre-quantized",
                    "M": M, "K": K, "N": N, "block": 128},
-        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+        "roofline": roofline, "cpu_baseline": cpu, "cpu_baselines": cpu_lines, "extra": extra,
     }
     print(json.dumps(out), flush=True)
 
 
-def gemm_traffic():
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary, if it
-    was taken on the current GEMM source; else None."""
-    p = os.path.join(ROOT, "profiles", "gemm_i8_attn_4096_pmc.json")
-    src = os.path.join(ROOT, "w8a8_rotated_int8_amd", "csrc", "gemm.hip")
+def source_hash(files):
+    """sha256 over the named kernel sources (csrc/), in the given order."""
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "w8a8_rotated_int8_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def counter_traffic(record, sources):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (profiles/<record>), if it was taken on the current source of the kernel;
+    else None."""
+    p = os.path.join(ROOT, "profiles", record)
     try:
         rec = json.load(open(p))
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if rec.get("gemm_source_sha256") == h:
+        if rec.get("source_sha256") == source_hash(sources):
             return rec.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         pass
@@ -346,10 +370,30 @@ def bench_embedding(cr, torch, dev, dev_normal, time_ms, wl):
     q_ms = time_ms(lambda: cr.quantize_weight(E, chunk_rows=CH, out=(qe, se)), 2, 10)
     q_bytes = V * D * 3 + 4 * V
     del E
-    ids = torch.from_numpy(wl.embed_ids(0)).to(dev)
+    ids0 = wl.embed_ids(0)
+    ids = torch.from_numpy(ids0).to(dev)
     out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
     l_ms = time_ms(lambda: cr.embedding_lookup(ids, qe, se, out=out), 5, 50)
     l_bytes = T * (4 + D + 4 + 2 * D)
+    # from HBM: each timed call follows a 1 GiB device fill (the last-level cache
+    # holds 256 MB) and uses the next of four id sets (the recipe's ids shifted by
+    # a quarter of the table each), timed alone with events on the stream
+    import numpy as np
+    id_sets = [torch.from_numpy(((ids0.astype(np.int64) + j * (V // 4)) % V).astype(np.int32)).to(dev)
+               for j in range(4)]
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    n_cold = 40
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_cold)]
+    for i, (e0, e1) in enumerate(evs):
+        flush.fill_(i & 255)
+        e0.record()
+        cr.embedding_lookup(id_sets[i % 4], qe, se, out=out)
+        e1.record()
+    torch.cuda.synchronize()
+    lc = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    lc_ms = lc[len(lc) // 2]
+    del flush, id_sets
     # torch's 1 GiB device-to-device copy, a reference rate for streaming reads
     # and writes with ordinary stores (the lookup's non-temporal stores beat it)
     src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
@@ -361,15 +405,22 @@ def bench_embedding(cr, torch, dev, dev_normal, time_ms, wl):
         "embed_quant_us": round(q_ms * 1e3, 1),
         "embed_quant_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
         "embed_quant_pct_hbm": round(100 * q_bytes / (q_ms * 1e-3) / 1e9 / 8000.0, 1),
-        "embed_lookup_us": round(l_ms * 1e3, 1),
-        "embed_lookup_GBps": round(l_bytes / (l_ms * 1e-3) / 1e9, 1),
-        "embed_lookup_pct_hbm": round(100 * l_bytes / (l_ms * 1e-3) / 1e9 / 8000.0, 1),
+        "embed_quant_traffic_bytes": counter_traffic("rotate_quant_embed_pmc.json",
+                                                     ["rotate_quant.hip", "span_quant.h", "common.h"]),
+        "embed_lookup_from_hbm_us": round(lc_ms * 1e3, 1),
+        "embed_lookup_from_hbm_GBps": round(l_bytes / (lc_ms * 1e-3) / 1e9, 1),
+        "embed_lookup_from_hbm_pct_hbm": round(100 * l_bytes / (lc_ms * 1e-3) / 1e9 / 8000.0, 1),
+        "embed_lookup_traffic_bytes": counter_traffic("embedding_lookup_pmc.json",
+                                                      ["dequant_lookup.hip", "common.h"]),
+        "embed_lookup_back_to_back_us": round(l_ms * 1e3, 1),
+        "embed_lookup_back_to_back_GBps": round(l_bytes / (l_ms * 1e-3) / 1e9, 1),
         "device_copy_GBps": round(c_GBps, 1),
         "embed_quant_pct_copy": round(100 * q_bytes / (q_ms * 1e-3) / 1e9 / c_GBps, 1),
-        "embed_lookup_pct_copy": round(100 * l_bytes / (l_ms * 1e-3) / 1e9 / c_GBps, 1),
+        "embed_lookup_from_hbm_pct_copy": round(100 * l_bytes / (lc_ms * 1e-3) / 1e9 / c_GBps, 1),
     }
     log(f"[bench] embedding quant {r['embed_quant_us']} us ({r['embed_quant_GBps']} GB/s), lookup "
-        f"{r['embed_lookup_us']} us ({r['embed_lookup_GBps']} GB/s); device copy {r['device_copy_GBps']} GB/s")
+        f"from HBM {r['embed_lookup_from_hbm_us']} us ({r['embed_lookup_from_hbm_GBps']} GB/s; "
+        f"back to back {r['embed_lookup_back_to_back_us']} us); device copy {r['device_copy_GBps']} GB/s")
     return r
 
 
@@ -443,14 +494,169 @@ def bench_packed(cr, torch, dev, dev_normal, time_ms, wl):
 
     t = time_ms(stream_pass, 1, 3)
     ops = 2 * 2.0 * T * N * K * L
+    wsb16 = torch.empty(cr.workspace_bytes(cr.OP_LINEAR_BWD_DX, T, N, K, cr.BWD_BF16),
+                        dtype=torch.uint8, device=dev)
+
+    def stream_pass_bf16():
+        for i in range(L):
+            cr.linear_fwd(x, qws[i], sws[i], out=y, workspace=wsf)
+            cr.linear_bwd_dx(dy, qws[i], sws[i], cr.BWD_BF16, out=dx, workspace=wsb16)
+
+    t16 = time_ms(stream_pass_bf16, 1, 3)
     r = {
         "packed_fwd_dx_int8_ms_per_pass": round(t, 2),
         "packed_tokens_per_s": round(T / (t * 1e-3), 0),
         "packed_tops": round(ops / (t * 1e-3) / 1e12, 1),
+        "packed_fwd_dx_bf16_ms_per_pass": round(t16, 2),
+        "packed_bf16_tokens_per_s": round(T / (t16 * 1e-3), 0),
+        "packed_bf16_tops": round(ops / (t16 * 1e-3) / 1e12, 1),
         "packed_weight_quant_ms_total": round(qt_ms, 2),
     }
     log(f"[bench] packed {r}")
     return r
+
+
+def bench_text_encoder_quant(cr, torch, dev, dev_normal, wl):
+    """The text encoder's load-time quantization pass: its 200 Linear layers (a
+    stand-in for their shapes, workloads.text_encoder_linear_shapes) and the
+    248320 x 4096 token embedding in 8192-row chunks, quantized back to back on
+    one stream, every weight resident beforehand (~16 GB of bf16)."""
+    shapes = wl.text_encoder_linear_shapes()
+    V, D, CH = wl.EMBED_V, wl.EMBED_D, wl.EMBED_CHUNK
+    log(f"[bench] text-encoder quantization pass: {len(shapes)} linears + [{V},{D}] embedding")
+    ws = [dev_normal(tuple(sh), wl.SIGMA_W, 3000 + i) for i, sh in enumerate(shapes)]
+    E = dev_normal((V, D), wl.SIGMA_W, 6)
+    qs = [(torch.empty(tuple(sh), dtype=torch.int8, device=dev),
+           torch.empty((sh[0],), dtype=torch.float32, device=dev)) for sh in shapes]
+    qe = torch.empty((V, D), dtype=torch.int8, device=dev)
+    se = torch.empty((V,), dtype=torch.float32, device=dev)
+
+    def qpass():
+        for w, out in zip(ws, qs):
+            cr.quantize_weight(w, out=out)
+        cr.quantize_weight(E, chunk_rows=CH, out=(qe, se))
+
+    qpass()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(3):
+        e0.record()
+        qpass()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    t = sorted(times)[1]
+    nbytes = sum(a * b * 3 + 4 * a for a, b in shapes) + V * D * 3 + 4 * V
+    r = {"te_quant_pass_ms": round(t, 2), "te_quant_pass_GBps": round(nbytes / (t * 1e-3) / 1e9, 1),
+         "te_quant_pass_pct_hbm": round(100 * nbytes / (t * 1e-3) / 1e9 / 8000.0, 1),
+         "te_quant_pass_bytes": nbytes}
+    log(f"[bench] text-encoder quantization {r}")
+    del ws, E, qs, qe, se
+    torch.cuda.empty_cache()
+    return r
+
+
+def cpu_baselines(wl):
+    """The oracle (unmodified) on the other workloads, on bounded samples so that
+    the whole set takes seconds; each line states its sample and scaling."""
+    import numpy as np
+
+    import oracle
+    nthr = oracle.num_threads()
+    out = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    # tiny layer: forward + both input gradients in full, median of 20 runs
+    t = wl.tiny(0)
+    oq, os_, _ = oracle.rotate_quantize(t["w"])
+    ops1 = 3 * 2.0 * t["M"] * t["N"] * t["K"]
+
+    def c1():
+        oracle.linear_fwd(t["x"], oq, os_)
+        oracle.bwd_dx_int8(t["dy"], oq, os_)
+        oracle.bwd_dx_bf16(t["dy"], oq, os_)
+
+    for threads in (nthr, 1):
+        oracle.set_num_threads(threads)
+        ts = sorted(timed(c1) for _ in range(20))
+        dt = ts[10]
+        out[f"tiny_{threads}thr"] = {
+            "value": round(ops1 / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "ms": round(dt * 1e3, 3),
+            "sample": "tiny layer in full (x [64,256], W [256,256]): forward + int8 dX + bf16 dX, "
+                      "median of 20 runs"}
+    oracle.set_num_threads(nthr)
+
+    # MLP pair: 256 of the 4096 tokens through both forwards and both int8
+    # gradients (weights quantized beforehand, not timed)
+    rows = 64
+    x = wl.activations(4096, 4096, wl.n_outliers(4096), base=0)[:rows]
+    w = wl.mlp_weights(0)
+    h = wl.mlp_down_input(x, w["w_up"])
+    g = wl.mlp_grads(4096, 0)
+    qu, su, _ = oracle.rotate_quantize(w["w_up"])
+    qd, sd, _ = oracle.rotate_quantize(w["w_down"])
+    del w
+
+    def c3():
+        oracle.linear_fwd(x, qu, su)
+        oracle.linear_fwd(h, qd, sd)
+        oracle.bwd_dx_int8(g["dy_down"][:rows], qd, sd)
+        oracle.bwd_dx_int8(g["dy_up"][:rows], qu, su)
+
+    dt = timed(c3)
+    ops3 = 4 * 2.0 * rows * 4096 * 16384
+    out["mlp_pair"] = {
+        "value": round(ops3 / dt / 1e12, 6), "unit": "TOPS", "cores": nthr, "kind": "oracle",
+        "seconds": round(dt, 2),
+        "sample": f"MLP pair, {rows} of the 4096 tokens: up and down forwards + int8 dX of both "
+                  "(rate per token is independent of the token count)"}
+    del qu, su, qd, sd, h, g
+
+    # packed stream: one layer's forward + int8 dX on 256 of the 20480 tokens,
+    # extrapolated to the 252-layer pass over all tokens
+    p = wl.packed(0)
+    xs, dys = p["x"][:rows], p["dy"][:rows]
+    del p
+    w0 = wl.packed_weight(0, 0)
+    q0, s0, _ = oracle.rotate_quantize(w0)
+
+    def c4():
+        oracle.linear_fwd(xs, q0, s0)
+        oracle.bwd_dx_int8(dys, q0, s0)
+
+    dt = timed(c4)
+    scale = (20480 / rows) * 252
+    out["packed_stream_extrapolated"] = {
+        "value": round(20480 / (dt * scale), 3), "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+        "seconds_per_pass_extrapolated": round(dt * scale, 1), "extrapolated": True,
+        "sample": f"one layer's forward + int8 dX on {rows} of the 20480 packed tokens, "
+                  f"x {scale:.0f} for the 252-layer pass"}
+
+    # embedding: quantize one 8192-row chunk; look up 4096 ids in that chunk
+    E = wl.embed_table(0, V=8192)
+    dt = timed(lambda: oracle.rotate_quantize(E))
+    qb = 8192 * 4096 * 3 + 4 * 8192
+    out["embed_quant_chunk"] = {
+        "value": round(qb / dt / 1e9, 3), "unit": "GB/s", "cores": nthr, "kind": "oracle",
+        "seconds": round(dt, 2),
+        "sample": "one 8192-row chunk of the 248320 x 4096 embedding (31 such chunks)"}
+    qe, se, _ = oracle.rotate_quantize(E)
+    ids = wl.token_ids(4096, 8192, base=0)
+    dt = timed(lambda: oracle.embedding_lookup(ids, qe, se))
+    lb = 4096 * (4 + 4096 + 4 + 2 * 4096)
+    out["embed_lookup"] = {
+        "value": round(lb / dt / 1e9, 3), "unit": "GB/s", "cores": nthr, "kind": "oracle",
+        "seconds": round(dt, 2),
+        "sample": "4096 ids into one quantized 8192-row chunk (the workload looks up 32768)"}
+    log(f"[bench] CPU oracle lines: " + ", ".join(f"{k} {v['value']} {v['unit']}"
+                                                   for k, v in out.items()))
+    return out
 
 
 def cpu_baseline(a):

@@ -18,8 +18,11 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers to caller-owned memory, row-major and
- *     contiguous, 16-byte aligned.  bf16 values are passed as uint16_t bit patterns.
- *     Scales are fp32 and are never cast.
+ *     contiguous, 16-byte aligned (the lookup's oob_count: 4-byte aligned), bias
+ *     included when given; a misaligned pointer is CONVROT_EINVAL.  bf16 values
+ *     are passed as uint16_t bit patterns.  Scales are fp32 and are never cast.
+ *   - Size limits: every row, column, token or id count is at most 2^31 - 1 and
+ *     every tensor holds at most 2^40 elements (CONVROT_ESHAPE otherwise).
  *   - The rotation R = diag(H_128 / sqrt(128)) acts along the contraction axis;
  *     H_128 is the Sylvester Hadamard matrix in natural order.  block must be 128;
  *     the contraction length (K, or D for the embedding) must be a multiple of 128.
@@ -74,9 +77,11 @@ extern "C" {
  * Load-time weight quantization ("ConvRot INT8" in the training guide section 7.1;
  * row-wise quantization and row-chunked embedding quantization in the pull
  * request's Summary).  For every row of w [rows, cols]: rotate r = w_row * R
- * (the rotation sum is exact; r = fl32(fl64(sum) * c), c = 1/sqrt(128) in fp64),
+ * (r = fl32(fl64(sum) * c), c = 1/sqrt(128) in fp64; the binary64 sum is exact
+ * while a 128-block's magnitude spread stays under about 2^38),
  * a = max |r|, scale = fl32(a / 127), codes = round-half-even(fl32(r / scale))
- * in [-127, 127].  An all-zero row gets scale 0 and codes 0.
+ * clamped to [-127, 127].  A row whose scale is 0 (all zero, or a maximum below
+ * 127 * 2^-150, where a / 127 underflows) gets codes 0.
  *   w      bf16 [rows, cols], cols % 128 == 0, cols <= CONVROT_MAX_ROW_LEN
  *   block  must be 128
  *   chunk_rows  rows per launch (0 = all rows at once); results do not depend on it
@@ -148,15 +153,15 @@ int convrot_linear_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, const int8_t
  * rotated basis; the lookup dequantizes and applies the inverse rotation):
  * out[t] = bf16( (s_E[id] * q_E[id]) * R ).  An id outside [0, V) produces a zero
  * row and, if oob_count is non-NULL, atomically increments *oob_count (device
- * int32, not cleared by the call).
+ * int32, 4-byte aligned, not cleared by the call).
  *   ids int32 [T];  qe int8 [V, D];  se fp32 [V];  out bf16 [T, D]; D % 128 == 0
  */
 int convrot_embedding_lookup(const int32_t* ids, int64_t T, const int8_t* qe, const float* se,
                              int64_t V, int64_t D, uint16_t* out, int32_t* oob_count,
                              hipStream_t stream);
 
-/* Workspace bytes needed by an operation (0 on invalid sizes, and for an empty
- * batch, which needs none). */
+/* Workspace bytes needed by an operation (0 on invalid sizes or sizes over the
+ * limits, and for an empty batch, which needs none). */
 size_t convrot_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t mode);
 
 /* Human-readable text of a status code (static storage). */

@@ -55,6 +55,8 @@ def lib():
         L.oracle_rne_integer.restype = C.c_double
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = C.c_int
+        L.oracle_set_num_threads.argtypes = [C.c_int]
+        L.oracle_set_num_threads.restype = None
         for name in ("oracle_hadamard", "oracle_rotate_rows", "oracle_quantize_rows",
                      "oracle_rotate_quantize", "oracle_gemm_i8_i32", "oracle_dequant_epilogue",
                      "oracle_bwd_quant_dy", "oracle_gemm_i8_i32_rows_of_b",
@@ -321,6 +323,12 @@ def embedding_lookup(ids, qe, se, block: int = BLOCK):
 def num_threads() -> int:
     """Threads the oracle's OpenMP loops use."""
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the following oracle calls (timings only; results do not
+    depend on the thread count)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def double_to_bf16(x: float) -> int:

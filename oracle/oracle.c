@@ -33,8 +33,9 @@
  *   round-half-to-even of the IEEE fp32 quotient r / s, clamped to [-127,127];
  *   Sylvester natural-order Hadamard, normalised by 1/sqrt(block) applied to
  *   the rotated values; the rotation sum is carried out exactly (fp64) and the
- *   product with the constant is rounded to fp64 then to fp32; an all-zero row
- *   has scale 0 and codes 0.
+ *   product with the constant is rounded to fp64 then to fp32; a row whose
+ *   scale is 0 (all zero, or a maximum so small that a / 127 underflows) has
+ *   codes 0.
  *
  * Floating-point environment: built with -O2 -fno-fast-math -ffp-contract=off,
  * so every expression below rounds exactly as written.
@@ -182,12 +183,15 @@ static void quantize_one_row(const float* r, int64_t cols, int8_t* q, float* s_o
         float v = fabsf(r[j]);
         if (v > a) a = v;
     }
-    if (a == 0.0f) {
+    float s = a / 127.0f; /* IEEE binary32 division */
+    /* A zero scale dequantizes every code to 0 and leaves r / s undefined: the
+     * all-zero row, and a row whose maximum is so small (below 127 * 2^-150)
+     * that a / 127 underflows to 0, both get scale 0 and codes 0. */
+    if (s == 0.0f) {
         *s_out = 0.0f;
         for (int64_t j = 0; j < cols; ++j) q[j] = 0;
         return;
     }
-    float s = a / 127.0f; /* IEEE binary32 division */
     *s_out = s;
     for (int64_t j = 0; j < cols; ++j) {
         float t = r[j] / s; /* IEEE binary32 division */
@@ -494,8 +498,10 @@ int oracle_lora_epilogue(const int32_t* acc, int64_t nrows, int64_t N, const flo
     return ORACLE_OK;
 }
 
-/* Threads the OpenMP loops above use (reported with oracle timings). */
+/* Threads the OpenMP loops above use (reported with oracle timings), and a
+ * setter so that a timing can run single-threaded; results do not depend on it. */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+void oracle_set_num_threads(int n) { if (n > 0) omp_set_num_threads(n); }
 
 /* Rounding helpers exported for the oracle's own pins. */
 uint16_t oracle_double_to_bf16(double x) { return double_to_bf16(x); }

@@ -59,3 +59,45 @@ def assert_rows_close(gpu_bits: np.ndarray, ref_bits: np.ndarray, what: str, tol
     worst = int(np.argmax(e))
     assert np.all(e <= tol), f"{what}: row {worst} relative error {e[worst]:.3e} > {tol}"
     return float(e.max())
+
+
+def assert_fwd_elementwise(gpu_bits: np.ndarray, ref_bits: np.ndarray, what: str):
+    """Forward outputs without bias, element by element: the GPU's fp32 chain
+    fl32(fl32(fl32(acc) * s_x) * s_w) is within 3 * 2^-24 (relative) of the exact
+    product, so after both sides round to bf16 they differ by at most one bf16
+    ulp of the reference, i.e. |gpu - ref| <= 2^-7 * |ref|; an exact zero stays
+    zero."""
+    assert gpu_bits.shape == ref_bits.shape, (what, gpu_bits.shape, ref_bits.shape)
+    g = wl.bf16_bits_to_f32(gpu_bits).astype(np.float64)
+    r = wl.bf16_bits_to_f32(ref_bits).astype(np.float64)
+    bad = np.argwhere(np.abs(g - r) > 2.0 ** -7 * np.abs(r) + 1e-37)
+    assert bad.size == 0, (f"{what}: {len(bad)} elements beyond one bf16 ulp, first "
+                           f"{bad[:3].tolist()}")
+
+
+CANARY = 0x5A
+
+
+class Guarded:
+    """A device tensor with canary bands of ``band`` bytes on both sides, to
+    catch writes past either end of an output.  ``t`` is the tensor handed to
+    the kernels (16-byte aligned: the band is a multiple of 256 bytes)."""
+
+    def __init__(self, shape, dtype, band: int = 4096):
+        assert band % 256 == 0
+        n = int(np.prod(shape)) if len(shape) else 1
+        self.nbytes = n * torch.empty((), dtype=dtype).element_size()
+        self.band = band
+        self.raw = torch.full((band + self.nbytes + band,), CANARY, dtype=torch.uint8, device=dev())
+        self.t = self.raw[band:band + self.nbytes].view(dtype).view(*shape)
+
+    def check(self, what: str):
+        torch.cuda.synchronize()
+        lo = self.raw[:self.band]
+        hi = self.raw[self.band + self.nbytes:]
+        assert bool((lo == CANARY).all()), f"{what}: bytes before the buffer were written"
+        assert bool((hi == CANARY).all()), f"{what}: bytes after the buffer were written"
+
+
+def guarded_workspace(nbytes: int, band: int = 4096) -> Guarded:
+    return Guarded((max(nbytes, 256),), torch.uint8, band)

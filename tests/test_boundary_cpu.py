@@ -152,3 +152,102 @@ def test_binding_fails_loudly_without_library(cr, monkeypatch, tmp_path):
     monkeypatch.setattr(cr, "library_path", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         cr.lib()
+
+
+def _odd(p, by=4):
+    return C.c_void_p(p.value + by)
+
+
+def test_every_pointer_alignment_is_checked(cr):
+    """Each pointer the header promises 16-byte aligned is checked: the same
+    call with one pointer moved by 4 bytes is CONVROT_EINVAL (and nothing is
+    launched: the addresses are fake and there is no GPU)."""
+    L = cr.lib()
+    WS1 = 1 << 20
+    # (function, args with each pointer a placeholder name)
+    calls = {
+        "convrot_quantize_weight": (["w", 64, 256, 128, 0, "q", "s", None], ["w", "q", "s"]),
+        "convrot_quantize_act": (["x", 64, 256, "q", "s", None], ["x", "q", "s"]),
+        "convrot_bwd_quant_dy": (["dy", 64, 256, "sw", "q", "s", None], ["dy", "sw", "q", "s"]),
+        "convrot_gemm_i8_bf16": (["qx", "sx", "qw", "sw", 64, 256, 256, "bias", "y", None],
+                                 ["qx", "sx", "qw", "sw", "bias", "y"]),
+        "convrot_linear_fwd": (["x", 64, 256, "qw", "sw", 256, "bias", "y", "ws", WS1, None],
+                               ["x", "qw", "sw", "bias", "y"]),
+        "convrot_linear_fwd_lora": (["x", 64, 256, "qw", "sw", 256, "bias", "a", "b", 16, 1.0, "y",
+                                     "ws", WS1, None], ["x", "qw", "sw", "bias", "a", "b", "y"]),
+        "convrot_lora_down": (["x", 64, 256, "a", 16, "xa", None], ["x", "a", "xa"]),
+        "convrot_gemm_i8_i32": (["a", "b", 64, 256, 256, 0, "acc", None], ["a", "b", "acc"]),
+        "convrot_dequant_weight_t": (["qw", "sw", 256, 256, "wt", None], ["qw", "sw", "wt"]),
+        "convrot_linear_bwd_dx": (["dy", 64, 256, "qw", "sw", 256, 1, "dx", "ws", WS1, None],
+                                  ["dy", "qw", "sw", "dx"]),
+        "convrot_embedding_lookup": (["ids", 64, "qe", "se", 1000, 256, "out", "oob", None],
+                                     ["ids", "qe", "se", "out"]),
+    }
+    base = {}
+    for i, name in enumerate(sorted({a for args, _ in calls.values() for a in args
+                                     if isinstance(a, str)})):
+        base[name] = C.c_void_p((i + 1) << 24)
+    assert set(calls) | {"convrot_workspace_bytes", "convrot_status_string"} == set(cr.EXPORTS)
+    for fn, (args, ptrs) in calls.items():
+        f = getattr(L, fn)
+        for moved in ptrs:
+            real = [(_odd(base[a]) if a == moved else base[a]) if isinstance(a, str) else a
+                    for a in args]
+            assert f(*real) == -1, (fn, moved)
+    # the workspace must be 256-byte aligned, the lookup's counter 4-byte aligned
+    for fn in ("convrot_linear_fwd", "convrot_linear_fwd_lora", "convrot_linear_bwd_dx"):
+        args, _ = calls[fn]
+        real = [(_odd(base[a], 128) if a == "ws" else base[a]) if isinstance(a, str) else a
+                for a in args]
+        assert getattr(L, fn)(*real) == -1, fn
+    args, _ = calls["convrot_embedding_lookup"]
+    real = [(_odd(base[a], 2) if a == "oob" else base[a]) if isinstance(a, str) else a
+            for a in args]
+    assert L.convrot_embedding_lookup(*real) == -1
+
+
+def test_size_limits(cr):
+    """Row, column and id counts above 2^31 - 1, or tensors above 2^40 elements,
+    are CONVROT_ESHAPE before any size arithmetic could overflow; the workspace
+    query returns 0 for them."""
+    L = cr.lib()
+    big = (1 << 31)
+    assert L.convrot_quantize_act(A, big, 128, B, Y, None) == -2
+    assert L.convrot_quantize_act(A, (1 << 40) // 4096 + 1, 4096, B, Y, None) == -2
+    assert L.convrot_linear_fwd(A, 64, 4096, B, B, big, None, Y, WS, 1 << 20, None) == -2
+    assert L.convrot_gemm_i8_i32(A, B, 1 << 30, 1 << 30, 128, 0, Y, None) == -2
+    assert L.convrot_embedding_lookup(A, big, B, B, 10, 128, Y, None, None) == -2
+    assert L.convrot_linear_bwd_dx(A, 1 << 30, 1 << 20, B, B, 128, 0, Y, WS, 1 << 20, None) == -2
+    assert cr.workspace_bytes(cr.OP_LINEAR_FWD, big, 128, 128) == 0
+    assert cr.workspace_bytes(cr.OP_LINEAR_BWD_DX, 1 << 30, 1 << 30, 128, cr.BWD_BF16) == 0
+
+
+def test_activations_must_be_bf16(cr, monkeypatch):
+    """Activations and gradients keep their own dtype (bf16): the binding refuses
+    any other dtype before reaching the C ABI, so nothing is enqueued.  This is the
+    bug sd-scripts pull request 2461 lists first among the fixes of existing bugs:
+    activations cast to the int8 weight's dtype."""
+    import torch
+    calls = []
+
+    class Spy:
+        def __getattr__(self, name):
+            calls.append(name)
+            raise AssertionError(f"reached the C ABI: {name}")
+
+    monkeypatch.setattr(cr, "_lib", Spy())
+    qw = torch.zeros((256, 256), dtype=torch.int8)
+    sw = torch.ones(256, dtype=torch.float32)
+    la = torch.zeros((16, 256), dtype=torch.bfloat16)
+    lb = torch.zeros((256, 16), dtype=torch.bfloat16)
+    for dt in (torch.int8, torch.float16, torch.float32, torch.uint8):
+        x = torch.zeros((64, 256), dtype=dt)
+        for fn in (lambda: cr.linear_fwd(x, qw, sw), lambda: cr.quantize_act(x),
+                   lambda: cr.quantize_weight(x), lambda: cr.bwd_quant_dy(x, sw),
+                   lambda: cr.linear_bwd_dx(x, qw, sw, cr.BWD_INT8),
+                   lambda: cr.linear_bwd_dx(x, qw, sw, cr.BWD_BF16),
+                   lambda: cr.linear_fwd_lora(x, qw, sw, la, lb, 1.0),
+                   lambda: cr.lora_down(x, la)):
+            with pytest.raises(TypeError):
+                fn()
+    assert calls == []

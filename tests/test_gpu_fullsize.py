@@ -17,7 +17,8 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-from gpu_util import assert_exact, assert_rows_close, bf16_to_dev, bits, host, to_dev  # noqa: E402
+from gpu_util import (assert_exact, assert_fwd_elementwise, assert_rows_close, bf16_to_dev,  # noqa: E402
+                      bits, host, to_dev)
 
 
 @pytest.fixture(scope="module")
@@ -102,7 +103,9 @@ def test_mlp_forward(cr, orc, mlp, which):
     acc = cr.gemm_i8_i32(qx, qw, 0)
     oacc = orc.gemm_i8_i32(oqx, oq, rows)
     assert_exact(host(acc)[rows], oacc, "acc (sampled rows)")
-    e = assert_rows_close(bits(y)[rows], orc.dequant_epilogue(oacc, osx, os_, rows), "y")
+    oy = orc.dequant_epilogue(oacc, osx, os_, rows)
+    e = assert_rows_close(bits(y)[rows], oy, "y")
+    assert_fwd_elementwise(bits(y)[rows], oy, "y")
     say(f"  max row relerr {e:.2e}")
 
 
@@ -168,7 +171,7 @@ def test_packed_activation_quantization(cr, packed):
 @pytest.mark.parametrize("layer", [0, 251, 97, 180])
 def test_packed_layer(cr, orc, packed, layer):
     p = packed["p"]
-    say(f"packed: layer {layer} forward + int8 dX on 20480 tokens")
+    say(f"packed: layer {layer} forward + int8 and bf16 dX on 20480 tokens")
     w = wl.packed_weight(layer, 0)
     oq, os_, _ = orc.rotate_quantize(w)
     qw, sw = cr.quantize_weight(bf16_to_dev(w))
@@ -181,7 +184,9 @@ def test_packed_layer(cr, orc, packed, layer):
     acc = cr.gemm_i8_i32(qx, qw, 0)
     oacc = orc.gemm_i8_i32(packed["oqx"], oq, rows)
     assert_exact(host(acc)[rows], oacc, "acc")
-    assert_rows_close(bits(y)[rows], orc.dequant_epilogue(oacc, packed["osx"], os_, rows), "y")
+    oy = orc.dequant_epilogue(oacc, packed["osx"], os_, rows)
+    assert_rows_close(bits(y)[rows], oy, "y")
+    assert_fwd_elementwise(bits(y)[rows], oy, "y")
     dyd = bf16_to_dev(p["dy"])
     dx = cr.linear_bwd_dx(dyd, qw, sw, cr.BWD_INT8)
     qg, sg = cr.bwd_quant_dy(dyd, sw)
@@ -192,6 +197,11 @@ def test_packed_layer(cr, orc, packed, layer):
     oacc2 = orc.gemm_i8_i32_rows_of_b(oqg, oq, rows)
     assert_exact(host(acc2)[rows], oacc2, "acc2")
     assert_rows_close(bits(dx)[rows], orc.bwd_int8_epilogue(oacc2, osg, rows), "dX int8")
+    # the default backward: transient bf16 W_hat, bf16 GEMM over the 20480 tokens
+    dx16 = cr.linear_bwd_dx(dyd, qw, sw, cr.BWD_BF16)
+    owhat = orc.dequant_weight(oq, os_)
+    e = assert_rows_close(bits(dx16)[rows], orc.bf16_gemm_dx(p["dy"], owhat, rows), "dX bf16")
+    say(f"  bf16 dX max row relerr {e:.2e}")
 
 
 # --------------------------------------------------------------------------

@@ -19,7 +19,8 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-from gpu_util import assert_exact, assert_rows_close, bf16_to_dev, bits, host  # noqa: E402
+from gpu_util import (assert_exact, assert_fwd_elementwise, assert_rows_close, bf16_to_dev,  # noqa: E402
+                      bits, host)
 
 
 @pytest.fixture(scope="module")
@@ -75,5 +76,7 @@ def test_stacked_vs_oracle(cr, qkv):
     acc = cr.gemm_i8_i32(qx, qkv["qcat"], 0)
     oacc = oracle.gemm_i8_i32(oqx, oq, rows)
     assert_exact(host(acc)[rows], oacc, "stacked acc (sampled rows)")
-    e = assert_rows_close(bits(y)[rows], oracle.dequant_epilogue(oacc, osx, os_, rows), "stacked y")
+    oy = oracle.dequant_epilogue(oacc, osx, os_, rows)
+    e = assert_rows_close(bits(y)[rows], oy, "stacked y")
+    assert_fwd_elementwise(bits(y)[rows], oy, "stacked y")
     print(f"  max row relerr {e:.2e}", flush=True)

@@ -32,8 +32,9 @@ def orc():
     return oracle
 
 
-from gpu_util import (assert_exact, assert_rows_close, bf16_to_dev, bits, host,  # noqa: E402
-                      to_dev)
+from crafted import tiny_fold_rows  # noqa: E402
+from gpu_util import (Guarded, assert_exact, assert_fwd_elementwise, assert_rows_close,  # noqa: E402
+                      bf16_to_dev, bits, guarded_workspace, host, to_dev)
 
 
 def say(*a):
@@ -74,7 +75,10 @@ def test_quantize_act_exact(cr, orc, M, K):
     say(f"quantize_act M={M} K={K}")
     x = wl.activations(M, K, max(1, wl.n_outliers(K)), base=M + K)
     x = np.concatenate([x, crafted_rows(K)])
-    q, s = cr.quantize_act(bf16_to_dev(x))
+    gq, gs = Guarded(x.shape, torch.int8), Guarded((x.shape[0],), torch.float32)
+    q, s = cr.quantize_act(bf16_to_dev(x), out=(gq.t, gs.t))
+    gq.check("codes")
+    gs.check("scales")
     oq, os_, bad = orc.rotate_quantize(x)
     assert bad == 0
     assert_exact(host(s), os_, "scales")
@@ -142,7 +146,13 @@ def test_gemm_i32_rows_of_b_exact(cr, orc, M, N, K):
 
 def _fwd_case(cr, orc, x, w, bias=None, rows=None):
     qw, sw = cr.quantize_weight(bf16_to_dev(w))
-    y = cr.linear_fwd(bf16_to_dev(x), qw, sw, None if bias is None else bf16_to_dev(bias))
+    M, N = x.shape[0], w.shape[0]
+    gy = Guarded((M, N), torch.bfloat16)
+    gws = guarded_workspace(cr.workspace_bytes(cr.OP_LINEAR_FWD, M, N, x.shape[1]))
+    y = cr.linear_fwd(bf16_to_dev(x), qw, sw, None if bias is None else bf16_to_dev(bias),
+                      out=gy.t, workspace=gws.t)
+    gy.check("y")
+    gws.check("workspace")
     oqw, osw, _ = orc.rotate_quantize(w)
     ref = orc.linear_fwd(x, oqw, osw, bias=bias, rows=rows)
     yb = bits(y)
@@ -172,6 +182,7 @@ def test_linear_fwd_ragged(cr, orc, M, N, K):
     w = wl.normal_bf16((N, K), wl.SIGMA_W, M, 1)
     yb, ref = _fwd_case(cr, orc, x, w)
     assert_rows_close(yb, ref["y"], "y")
+    assert_fwd_elementwise(yb, ref["y"], "y")
 
 
 def test_linear_fwd_attn_full_size(cr, orc):
@@ -200,6 +211,7 @@ def test_linear_fwd_attn_full_size(cr, orc):
     assert_exact(host(acc)[rows], oacc, "acc (sampled rows)")
     oy = orc.dequant_epilogue(oacc, osx, osw, rows)
     e = assert_rows_close(bits(y)[rows], oy, "y (sampled rows)")
+    assert_fwd_elementwise(bits(y)[rows], oy, "y (sampled rows)")
     say(f"  max row relerr {e:.2e}")
 
 
@@ -236,12 +248,36 @@ def test_bwd_quant_dy_crafted_rows(cr, orc, N):
     assert_exact(host(qg), oqg, "q_g")
 
 
+@pytest.mark.parametrize("N", [256, 1152, 2048, 4096, 16384])
+def test_bwd_quant_dy_subnormal_scales(cr, orc, N):
+    # folded row maxima across fp32's subnormal binades: scales subnormal or zero,
+    # the maximum's quotient past 127.5 (clamped to 127), and (N = 4096) column
+    # scales that round the fold itself onto the subnormal grid
+    say(f"bwd_quant_dy subnormal scales N={N}")
+    dy, sw = tiny_fold_rows(N, N)
+    if N == 4096:
+        sw = (np.random.default_rng(2).uniform(0.5, 1.0, N) * 2.0 ** -20).astype(np.float32)
+    gq, gs = Guarded(dy.shape, torch.int8), Guarded((dy.shape[0],), torch.float32)
+    qg, sg = cr.bwd_quant_dy(bf16_to_dev(dy), torch.from_numpy(sw).cuda(), out=(gq.t, gs.t))
+    gq.check("q_g")
+    gs.check("s_g")
+    oqg, osg = orc.bwd_quant_dy(dy, sw)
+    assert (osg == 0).any() and ((osg > 0) & (osg < 2.0 ** -126)).any()
+    assert_exact(host(sg), osg, "s_g")
+    assert_exact(host(qg), oqg, "q_g")
+
+
 def _bwd_int8(cr, orc, dy, w, rows=None):
     qw, sw = cr.quantize_weight(bf16_to_dev(w))
     oqw, osw, _ = orc.rotate_quantize(w)
     dyd = bf16_to_dev(dy)
     qg, sg = cr.bwd_quant_dy(dyd, sw)
-    dx = cr.linear_bwd_dx(dyd, qw, sw, cr.BWD_INT8)
+    M, N, K = dy.shape[0], dy.shape[1], w.shape[1]
+    gdx = Guarded((M, K), torch.bfloat16)
+    gws = guarded_workspace(cr.workspace_bytes(cr.OP_LINEAR_BWD_DX, M, N, K, cr.BWD_INT8))
+    dx = cr.linear_bwd_dx(dyd, qw, sw, cr.BWD_INT8, out=gdx.t, workspace=gws.t)
+    gdx.check("dX int8")
+    gws.check("workspace (int8 dX)")
     oqg, osg = orc.bwd_quant_dy(dy, osw)
     assert_exact(host(sg), osg, "s_g")
     assert_exact(host(qg), oqg, "q_g")
@@ -257,10 +293,17 @@ def _bwd_int8(cr, orc, dy, w, rows=None):
 def _bwd_bf16(cr, orc, dy, w, rows=None):
     qw, sw = cr.quantize_weight(bf16_to_dev(w))
     oqw, osw, _ = orc.rotate_quantize(w)
-    wt = cr.dequant_weight_t(qw, sw)
+    gwt = Guarded((w.shape[1], w.shape[0]), torch.bfloat16)
+    wt = cr.dequant_weight_t(qw, sw, out=gwt.t)
+    gwt.check("W_hat^T")
     owhat = orc.dequant_weight(oqw, osw)
     assert_rows_close(bits(wt), np.ascontiguousarray(owhat.T), "W_hat^T")
-    dx = cr.linear_bwd_dx(bf16_to_dev(dy), qw, sw, cr.BWD_BF16)
+    M, N, K = dy.shape[0], dy.shape[1], w.shape[1]
+    gdx = Guarded((M, K), torch.bfloat16)
+    gws = guarded_workspace(cr.workspace_bytes(cr.OP_LINEAR_BWD_DX, M, N, K, cr.BWD_BF16))
+    dx = cr.linear_bwd_dx(bf16_to_dev(dy), qw, sw, cr.BWD_BF16, out=gdx.t, workspace=gws.t)
+    gdx.check("dX bf16")
+    gws.check("workspace (bf16 dX)")
     odx = orc.bf16_gemm_dx(dy, owhat, rows)
     dxb = bits(dx) if rows is None else bits(dx)[rows]
     return assert_rows_close(dxb, odx, "dX bf16")
@@ -303,7 +346,9 @@ def test_embedding_lookup(cr, orc, V, D, T):
     ids = wl.token_ids(T, V, base=D)
     ids[0], ids[-1] = -5, V   # out of range -> zero rows, counted
     oob = torch.zeros(1, dtype=torch.int32, device="cuda")
-    out = cr.embedding_lookup(to_dev(ids), qe, se, oob)
+    gout = Guarded((T, D), torch.bfloat16)
+    out = cr.embedding_lookup(to_dev(ids), qe, se, oob, out=gout.t)
+    gout.check("lookup")
     oout, ooob = orc.embedding_lookup(ids, oqe, ose)
     assert int(oob.item()) == ooob == 2
     ob = bits(out)

@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-from gpu_util import assert_exact, assert_rows_close, bf16_to_dev, bits, host  # noqa: E402
+from gpu_util import (Guarded, assert_exact, assert_fwd_elementwise, assert_rows_close,  # noqa: E402
+                      bf16_to_dev, bits, guarded_workspace, host)
 
 
 def _shapes():
@@ -66,7 +67,11 @@ def test_shape(cr, orc, M, N, K):
     w = wl.packed_weight(base % 997, base, N, K)
     qw, sw = cr.quantize_weight(bf16_to_dev(w))
     xd = bf16_to_dev(x)
-    y = cr.linear_fwd(xd, qw, sw)
+    gy = Guarded((M, N), torch.bfloat16)
+    gws = guarded_workspace(cr.workspace_bytes(cr.OP_LINEAR_FWD, M, N, K))
+    y = cr.linear_fwd(xd, qw, sw, out=gy.t, workspace=gws.t)
+    gy.check("y")
+    gws.check("workspace")
     qx, sx = cr.quantize_act(xd)
     assert torch.equal(y, cr.gemm_i8_bf16(qx, sx, qw, sw)), "forward differs from its stages"
 
@@ -78,12 +83,17 @@ def test_shape(cr, orc, M, N, K):
     assert_exact(host(qx)[rows], oqx, "q_x rows")
     assert_exact(host(sx)[rows], osx, "s_x rows")
     oacc = orc.gemm_i8_i32(oqx, oqw)
-    assert_rows_close(bits(y)[rows], orc.dequant_epilogue(oacc, osx, osw), "y rows")
+    oy = orc.dequant_epilogue(oacc, osx, osw)
+    assert_rows_close(bits(y)[rows], oy, "y rows")
+    assert_fwd_elementwise(bits(y)[rows], oy, "y rows")
 
     if N % 128 == 0:
         dy = wl.normal_bf16((M, N), 1e-3, base, 3)
         dyd = bf16_to_dev(dy)
-        dx8 = cr.linear_bwd_dx(dyd, qw, sw, cr.BWD_INT8)
-        dx16 = cr.linear_bwd_dx(dyd, qw, sw, cr.BWD_BF16)
+        gd8, gd16 = Guarded((M, K), torch.bfloat16), Guarded((M, K), torch.bfloat16)
+        dx8 = cr.linear_bwd_dx(dyd, qw, sw, cr.BWD_INT8, out=gd8.t)
+        dx16 = cr.linear_bwd_dx(dyd, qw, sw, cr.BWD_BF16, out=gd16.t)
+        gd8.check("int8 dX")
+        gd16.check("bf16 dX")
         assert_rows_close(bits(dx8)[rows], orc.bwd_dx_int8(dy[rows], oqw, osw)["dx"], "int8 dX rows")
         assert_rows_close(bits(dx16)[rows], orc.bwd_dx_bf16(dy[rows], oqw, osw)["dx"], "bf16 dX rows")

@@ -25,7 +25,8 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-from gpu_util import assert_exact, assert_rows_close, bf16_to_dev, bits, host  # noqa: E402
+from gpu_util import (Guarded, assert_exact, assert_fwd_elementwise, assert_rows_close,  # noqa: E402
+                      bf16_to_dev, bits, guarded_workspace, host)
 
 
 @pytest.fixture(scope="module")
@@ -66,7 +67,10 @@ def test_small_m_forward(cr, M, K, N):
           flush=True)
     qw, sw = cr.quantize_weight(bf16_to_dev(w))
     xd = bf16_to_dev(x)
-    y = cr.linear_fwd(xd, qw, sw)
+    gy, gws = Guarded((M, N), torch.bfloat16), guarded_workspace(need)
+    y = cr.linear_fwd(xd, qw, sw, out=gy.t, workspace=gws.t)
+    gy.check("y")
+    gws.check("workspace (q_x, s_x, partials)")
     qx, sx = cr.quantize_act(xd)
     y1 = cr.gemm_i8_bf16(qx, sx, qw, sw)
     assert torch.equal(y, y1), "split forward differs from the one-pass stages"
@@ -77,7 +81,9 @@ def test_small_m_forward(cr, M, K, N):
     assert_exact(host(qx)[rows], oqx, "q_x (sampled rows)")
     oacc = oracle.gemm_i8_i32(oqx, oqw)
     assert_exact(host(cr.gemm_i8_i32(qx, qw, 0))[rows], oacc, "acc (sampled rows)")
-    e = assert_rows_close(bits(y)[rows], oracle.dequant_epilogue(oacc, osx, osw), "y (sampled rows)")
+    oy = oracle.dequant_epilogue(oacc, osx, osw)
+    e = assert_rows_close(bits(y)[rows], oy, "y (sampled rows)")
+    assert_fwd_elementwise(bits(y)[rows], oy, "y (sampled rows)")
     print(f"  max row relerr {e:.2e}", flush=True)
 
 

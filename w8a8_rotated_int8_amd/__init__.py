@@ -164,12 +164,13 @@ def quantize_weight(w: torch.Tensor, block: int = BLOCK, chunk_rows: int = 0, ou
     return q, s
 
 
-def quantize_act(x: torch.Tensor):
+def quantize_act(x: torch.Tensor, out=None):
     """Online activation rotation + per-row quantization -> (q_x, s_x)."""
     _req(x, "x", torch.bfloat16, 2)
     M, K = x.shape
-    q = torch.empty((M, K), dtype=torch.int8, device=x.device)
-    s = torch.empty((M,), dtype=torch.float32, device=x.device)
+    q0, s0 = out if out is not None else (None, None)
+    q = _out(q0, "q", torch.int8, (M, K), x.device)
+    s = _out(s0, "scale", torch.float32, (M,), x.device)
     _call("convrot_quantize_act", _ptr(x), M, K, _ptr(q), _ptr(s), _stream())
     return q, s
 
@@ -262,14 +263,15 @@ def gemm_i8_i32(a, b, b_layout: int = 0, out=None):
     return acc
 
 
-def bwd_quant_dy(dy, sw):
+def bwd_quant_dy(dy, sw, out=None):
     """First stage of the int8 input gradient -> (q_g, s_g)."""
     _req(dy, "dy", torch.bfloat16, 2)
     _req(sw, "sw", torch.float32, 1)
     M, N = dy.shape
     _like(sw, "sw", torch.float32, (N,))
-    q = torch.empty((M, N), dtype=torch.int8, device=dy.device)
-    s = torch.empty((M,), dtype=torch.float32, device=dy.device)
+    q0, s0 = out if out is not None else (None, None)
+    q = _out(q0, "q", torch.int8, (M, N), dy.device)
+    s = _out(s0, "scale", torch.float32, (M,), dy.device)
     _call("convrot_bwd_quant_dy", _ptr(dy), M, N, _ptr(sw), _ptr(q), _ptr(s), _stream())
     return q, s
 
@@ -290,12 +292,12 @@ def linear_bwd_dx(dy, qw, sw, mode: int = BWD_BF16, out=None, workspace=None):
     return dx
 
 
-def dequant_weight_t(qw, sw):
+def dequant_weight_t(qw, sw, out=None):
     """Transient bf16 weight of the bf16 input gradient, transposed: [K, N]."""
     _req(qw, "qw", torch.int8, 2)
     N, K = qw.shape
     _like(sw, "sw", torch.float32, (N,))
-    out = torch.empty((K, N), dtype=torch.bfloat16, device=qw.device)
+    out = _out(out, "out", torch.bfloat16, (K, N), qw.device)
     _call("convrot_dequant_weight_t", _ptr(qw), _ptr(sw), N, K, _ptr(out), _stream())
     return out
 

@@ -7,6 +7,7 @@
 #include "../../include/convrot.h"
 #include "common.h"
 #include "kernels.h"
+#include "validate.h"
 
 namespace convrot {
 namespace {
@@ -28,25 +29,18 @@ int check_device() {
   return st == 1 ? CONVROT_OK : CONVROT_EDEVICE;
 }
 
-inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONVROT_EHIP; }
 
-bool row_len_ok(int64_t K) { return K > 0 && K % kBlock == 0 && K <= CONVROT_MAX_ROW_LEN; }
+// Status of the host-side checks (validate.h) as the entry point returns it:
+// an empty batch enqueues nothing and succeeds.
+inline int checked(int st) { return st == check::kNoOp ? CONVROT_OK : st; }
 
-// An empty batch (no rows, tokens or ids) enqueues nothing: only the other
-// sizes are checked, and the pointers are not looked at.
-inline int empty_batch(bool shape_ok) { return shape_ok ? CONVROT_OK : CONVROT_ESHAPE; }
-
-int quantize_rows_checked(const uint16_t* x, int64_t rows, int64_t K, int8_t* q, float* s,
-                          int64_t chunk_rows, const float* colscale, bool fold, bool weights,
-                          hipStream_t stream) {
-  if (rows == 0 && K > 0 && chunk_rows >= 0) return empty_batch(row_len_ok(K));
-  if (!x || !q || !s || rows <= 0 || K <= 0 || chunk_rows < 0) return CONVROT_EINVAL;
-  if (fold && !colscale) return CONVROT_EINVAL;
-  if (!aligned16(x) || !aligned16(q) || (colscale && !aligned16(colscale))) return CONVROT_EINVAL;
-  if (!row_len_ok(K)) return CONVROT_ESHAPE;
+// Rows already validated (check::quantize_rows).
+int quantize_rows_launch(const uint16_t* x, int64_t rows, int64_t K, int8_t* q, float* s,
+                         int64_t chunk_rows, const float* colscale, bool fold, bool weights,
+                         hipStream_t stream) {
   int st = check_device();
   if (st) return st;
   if (chunk_rows == 0 || chunk_rows > rows) chunk_rows = rows;
@@ -92,6 +86,7 @@ const char* convrot_status_string(int status) {
 
 size_t convrot_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t mode) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
+  if (!check::dims_ok(M, K) || !check::dims_ok(N, K) || !check::dims_ok(M, N)) return 0;
   if (op == CONVROT_OP_LINEAR_FWD) return fwd_workspace(M, K) + fwd_splitk_workspace(M, N, K);
   if (op == CONVROT_OP_LINEAR_FWD_LORA)
     return (mode == 16 || mode == 32) ? fwd_workspace(M, K) + align256(2 * (size_t)M * mode) : 0;
@@ -104,28 +99,31 @@ size_t convrot_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int3
 
 int convrot_quantize_weight(const uint16_t* w, int64_t rows, int64_t cols, int32_t block,
                             int64_t chunk_rows, int8_t* q, float* scale, hipStream_t stream) {
-  if (block != kBlock) return (rows == 0 || (w && q && scale)) ? CONVROT_ESHAPE : CONVROT_EINVAL;
-  return quantize_rows_checked(w, rows, cols, q, scale, chunk_rows, nullptr, false, true, stream);
+  int st = check::quantize_weight(w, rows, cols, block, chunk_rows, q, scale);
+  if (st) return checked(st);
+  return quantize_rows_launch(w, rows, cols, q, scale, chunk_rows, nullptr, false, true, stream);
 }
 
 int convrot_quantize_act(const uint16_t* x, int64_t M, int64_t K, int8_t* qx, float* sx,
                          hipStream_t stream) {
-  return quantize_rows_checked(x, M, K, qx, sx, 0, nullptr, false, false, stream);
+  int st = check::quantize_rows(x, M, K, qx, sx, 0, nullptr, false);
+  if (st) return checked(st);
+  return quantize_rows_launch(x, M, K, qx, sx, 0, nullptr, false, false, stream);
 }
 
 int convrot_bwd_quant_dy(const uint16_t* dy, int64_t M, int64_t N, const float* sw, int8_t* qg,
                          float* sg, hipStream_t stream) {
-  return quantize_rows_checked(dy, M, N, qg, sg, 0, sw, true, false, stream);
+  int st = check::quantize_rows(dy, M, N, qg, sg, 0, sw, true);
+  if (st) return checked(st);
+  return quantize_rows_launch(dy, M, N, qg, sg, 0, sw, true, false, stream);
 }
 
 int convrot_gemm_i8_bf16(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw,
                          int64_t M, int64_t N, int64_t K, const uint16_t* bias, uint16_t* y,
                          hipStream_t stream) {
-  if (M == 0 && N > 0 && K > 0) return empty_batch(K % kBlock == 0);
-  if (!qx || !sx || !qw || !sw || !y || M <= 0 || N <= 0 || K <= 0) return CONVROT_EINVAL;
-  if (!aligned16(qx) || !aligned16(qw) || !aligned16(y)) return CONVROT_EINVAL;
-  if (K % kBlock) return CONVROT_ESHAPE;
-  int st = check_device();
+  int st = check::gemm_i8_bf16(qx, sx, qw, sw, M, N, K, bias, y);
+  if (st) return checked(st);
+  st = check_device();
   if (st) return st;
   GemmArgs a{};
   a.P = qw; a.Q = qx; a.I = N; a.J = M; a.Kc = K; a.ldp = K; a.ldq = K;
@@ -136,15 +134,11 @@ int convrot_gemm_i8_bf16(const int8_t* qx, const float* sx, const int8_t* qw, co
 int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw,
                        const float* sw, int64_t N, const uint16_t* bias, uint16_t* y,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (M == 0 && N > 0 && K > 0) return empty_batch(row_len_ok(K));
-  if (!x || !qw || !sw || !y || !workspace || M <= 0 || N <= 0 || K <= 0) return CONVROT_EINVAL;
-  if (!aligned16(x) || !aligned16(qw) || !aligned16(y) ||
-      (reinterpret_cast<uintptr_t>(workspace) & 255))
-    return CONVROT_EINVAL;
-  if (!row_len_ok(K)) return CONVROT_ESHAPE;
+  int st = check::linear_fwd(x, M, K, qw, sw, N, bias, y, workspace);
+  if (st) return checked(st);
   if (workspace_bytes < fwd_workspace(M, K) + fwd_splitk_workspace(M, N, K))
     return CONVROT_EWORKSPACE;
-  int st = check_device();
+  st = check_device();
   if (st) return st;
   int8_t* qx = static_cast<int8_t*>(workspace);
   float* sx = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + align256((size_t)M * K));
@@ -166,16 +160,11 @@ int convrot_linear_fwd_lora(const uint16_t* x, int64_t M, int64_t K, const int8_
                             const uint16_t* lora_a, const uint16_t* lora_b, int32_t R,
                             float lora_scale, uint16_t* y, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
-  if (M == 0 && N > 0 && K > 0) return empty_batch(row_len_ok(K) && (R == 16 || R == 32));
-  if (!x || !qw || !sw || !y || !lora_a || !lora_b || !workspace || M <= 0 || N <= 0 || K <= 0)
-    return CONVROT_EINVAL;
-  if (!aligned16(x) || !aligned16(qw) || !aligned16(y) || !aligned16(lora_a) ||
-      !aligned16(lora_b) || (reinterpret_cast<uintptr_t>(workspace) & 255))
-    return CONVROT_EINVAL;
-  if (!row_len_ok(K) || (R != 16 && R != 32)) return CONVROT_ESHAPE;
+  int st = check::linear_fwd_lora(x, M, K, qw, sw, N, bias, lora_a, lora_b, R, y, workspace);
+  if (st) return checked(st);
   const size_t xa_off = fwd_workspace(M, K);
   if (workspace_bytes < xa_off + align256(2 * (size_t)M * R)) return CONVROT_EWORKSPACE;
-  int st = check_device();
+  st = check_device();
   if (st) return st;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int8_t* qx = reinterpret_cast<int8_t*>(ws);
@@ -193,25 +182,18 @@ int convrot_linear_fwd_lora(const uint16_t* x, int64_t M, int64_t K, const int8_
 
 int convrot_lora_down(const uint16_t* x, int64_t M, int64_t K, const uint16_t* lora_a,
                       int32_t R, uint16_t* xa, hipStream_t stream) {
-  if (M == 0 && K > 0) return empty_batch(row_len_ok(K) && (R == 16 || R == 32));
-  if (!x || !lora_a || !xa || M <= 0 || K <= 0) return CONVROT_EINVAL;
-  if (!aligned16(x) || !aligned16(lora_a)) return CONVROT_EINVAL;
-  if (!row_len_ok(K) || (R != 16 && R != 32)) return CONVROT_ESHAPE;
-  int st = check_device();
+  int st = check::lora_down(x, M, K, lora_a, R, xa);
+  if (st) return checked(st);
+  st = check_device();
   if (st) return st;
   return hip_status(launch_lora_down(x, M, K, lora_a, R, xa, stream));
 }
 
 int convrot_gemm_i8_i32(const int8_t* a_, const int8_t* b, int64_t M, int64_t N, int64_t K,
                         int32_t b_layout, int32_t* acc, hipStream_t stream) {
-  if (M == 0 && N > 0 && K > 0 && (b_layout == 0 || b_layout == 1))
-    return empty_batch(K % kBlock == 0 && (b_layout == 0 || N % kBlock == 0));
-  if (!a_ || !b || !acc || M <= 0 || N <= 0 || K <= 0) return CONVROT_EINVAL;
-  if (!aligned16(a_) || !aligned16(b) || !aligned16(acc)) return CONVROT_EINVAL;
-  if (b_layout != 0 && b_layout != 1) return CONVROT_EINVAL;
-  if (K % kBlock) return CONVROT_ESHAPE;
-  if (b_layout == 1 && N % kBlock) return CONVROT_ESHAPE;
-  int st = check_device();
+  int st = check::gemm_i8_i32(a_, b, M, N, K, b_layout, acc);
+  if (st) return checked(st);
+  st = check_device();
   if (st) return st;
   GemmArgs a{};
   a.P = b; a.Q = a_; a.I = N; a.J = M; a.Kc = K; a.ldp = b_layout == 0 ? K : N; a.ldq = K;
@@ -221,10 +203,9 @@ int convrot_gemm_i8_i32(const int8_t* a_, const int8_t* b, int64_t M, int64_t N,
 
 int convrot_dequant_weight_t(const int8_t* qw, const float* sw, int64_t N, int64_t K,
                              uint16_t* what_t, hipStream_t stream) {
-  if (!qw || !sw || !what_t || N <= 0 || K <= 0) return CONVROT_EINVAL;
-  if (!aligned16(qw) || !aligned16(what_t)) return CONVROT_EINVAL;
-  if (K % kBlock) return CONVROT_ESHAPE;
-  int st = check_device();
+  int st = check::dequant_weight_t(qw, sw, N, K, what_t);
+  if (st) return checked(st);
+  st = check_device();
   if (st) return st;
   return hip_status(launch_dequant_weight_t(qw, sw, N, K, what_t, stream));
 }
@@ -232,19 +213,11 @@ int convrot_dequant_weight_t(const int8_t* qw, const float* sw, int64_t N, int64
 int convrot_linear_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, const int8_t* qw,
                           const float* sw, int64_t K, int32_t mode, uint16_t* dx,
                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (M == 0 && N > 0 && K > 0 && (mode == CONVROT_BWD_BF16 || mode == CONVROT_BWD_INT8))
-    return empty_batch(K % kBlock == 0 && N % kBlock == 0 &&
-                       (mode != CONVROT_BWD_INT8 || N <= CONVROT_MAX_ROW_LEN));
-  if (!dy || !qw || !sw || !dx || !workspace || M <= 0 || N <= 0 || K <= 0) return CONVROT_EINVAL;
-  if (mode != CONVROT_BWD_BF16 && mode != CONVROT_BWD_INT8) return CONVROT_EINVAL;
-  if (!aligned16(dy) || !aligned16(qw) || !aligned16(sw) || !aligned16(dx) ||
-      (reinterpret_cast<uintptr_t>(workspace) & 255))
-    return CONVROT_EINVAL;
-  if (K % kBlock || N % kBlock) return CONVROT_ESHAPE;
-  if (mode == CONVROT_BWD_INT8 && N > CONVROT_MAX_ROW_LEN) return CONVROT_ESHAPE;
+  int st = check::linear_bwd_dx(dy, M, N, qw, sw, K, mode, dx, workspace);
+  if (st) return checked(st);
   if (workspace_bytes < convrot_workspace_bytes(CONVROT_OP_LINEAR_BWD_DX, M, N, K, mode))
     return CONVROT_EWORKSPACE;
-  int st = check_device();
+  st = check_device();
   if (st) return st;
   if (mode == CONVROT_BWD_INT8) {
     int8_t* qg = static_cast<int8_t*>(workspace);
@@ -268,11 +241,9 @@ int convrot_linear_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, const int8_t
 int convrot_embedding_lookup(const int32_t* ids, int64_t T, const int8_t* qe, const float* se,
                              int64_t V, int64_t D, uint16_t* out, int32_t* oob_count,
                              hipStream_t stream) {
-  if (T == 0 && V > 0 && D > 0) return empty_batch(D % kBlock == 0);
-  if (!ids || !qe || !se || !out || T <= 0 || V <= 0 || D <= 0) return CONVROT_EINVAL;
-  if (!aligned16(qe) || !aligned16(out)) return CONVROT_EINVAL;
-  if (D % kBlock) return CONVROT_ESHAPE;
-  int st = check_device();
+  int st = check::embedding_lookup(ids, T, qe, se, V, D, out, oob_count);
+  if (st) return checked(st);
+  st = check_device();
   if (st) return st;
   return hip_status(launch_embedding_lookup(ids, T, qe, se, V, D, out, oob_count, stream));
 }

@@ -265,7 +265,9 @@ hipError_t launch_embedding_lookup(const int32_t* ids, int64_t T, const int8_t* 
     if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     int64_t grid = (T + 3) / 4;
-    const int64_t cap = 4 * (int64_t)n_cu;  // four resident workgroups per CU
+    // at most four workgroups per CU: two are resident at a time (64 KB of LDS
+    // each), the other two start as those finish
+    const int64_t cap = 4 * (int64_t)n_cu;
     if (grid > cap) grid = cap;
     hipLaunchKernelGGL(embedding_lookup_kernel, dim3((unsigned)grid), dim3(256), 0, stream, ids,
                        T, qe, se, V, (int)D, out, oob);

@@ -128,11 +128,16 @@ __global__ __launch_bounds__(1024) void fold_quant_rows_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) t[j][e] = quot_rn(r[j][e], s, inv);
   } else {
+    // Extreme rows: IEEE division.  When s is subnormal its rounding error can
+    // push |t| past 127.5 (a folded maximum of 2^-140 gives s = 2^-147 and
+    // t = 128), so the codes are clamped to [-127, 127]; a zero s (a/127
+    // underflowed) gives codes 0.
     s = m / 127.0f;
 #pragma unroll
     for (int j = 0; j < kFoldUnits; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) t[j][e] = s > 0.f ? r[j][e] / s : 0.f;
+      for (int e = 0; e < 4; ++e)
+        t[j][e] = s > 0.f ? fminf(fmaxf(r[j][e] / s, -127.0f), 127.0f) : 0.f;
   }
   uint32_t* dst = reinterpret_cast<uint32_t*>(q + row * (int64_t)N);
 #pragma unroll

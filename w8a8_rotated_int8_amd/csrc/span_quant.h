@@ -2,15 +2,19 @@
 // quantization of a span of up to SB (16 or 32) consecutive 128-blocks held in
 // LDS, used by the row quantizer kernels.
 //
-// Arithmetic (bit-exact by construction):
+// Arithmetic:
 //   rotate:   per 128-block, S_j = sum_i H[i][j] x_i computed by a fast
-//             Walsh-Hadamard transform in binary64.  bf16 inputs make every
-//             partial sum exact (a block's magnitude spread would have to exceed
-//             2^38 before binary64 rounds), so the butterfly order cannot change
-//             the result; r_j = fl32(fl64(S_j * c)), c = 1/sqrt(128).
+//             Walsh-Hadamard transform in binary64; r_j = fl32(fl64(S_j * c)),
+//             c = 1/sqrt(128).  Every partial sum of bf16 inputs is exact, and
+//             the butterfly order cannot change the result, as long as a block's
+//             magnitude spread (largest over smallest nonzero |x_i|) stays under
+//             about 2^38.  Past that, binary64 rounds some partial sums and the
+//             result may depend on the order of the additions (GELU outputs near
+//             -inf reach such spreads; a host emulation of this butterfly order
+//             checks those rows against the index-order sum).
 //   fold:     (dY quantizer) r_n = fl32(fl32(dY_n) * s_w[n]); no rotation.
-//   quantize: a = max|r|, s = fl32(a/127), code = RNE(fl32(r/s)); all-zero row
-//             -> s = 0, codes 0.
+//   quantize: a = max|r|, s = fl32(a/127), code = clamp(RNE(fl32(r/s)), +-127);
+//             s = 0 (all-zero row, or a/127 underflowed) -> codes 0.
 //
 // Work layout.  A wave owns a span of SB blocks: several short rows packed
 // together, or an SB-block slice of a longer row (then the workgroup's waves
@@ -240,8 +244,14 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
     } else {
       s = m[k] / 127.0f;                               // IEEE binary32 division
       const float inv = s > 0.f ? 1.0f / s : 0.f;
+      // A subnormal s carries a relative rounding error that can push |t| past
+      // 127.5 (e.g. a = 2^-140: s = 2^-147, t = 128), so the codes are clamped
+      // to [-127, 127] here; a zero s (a/127 underflowed) gives codes 0.
 #pragma unroll
-      for (int e = 0; e < 32; ++e) t[e] = fast ? quot_rn(r[k][e], s, inv) : (s > 0.f ? r[k][e] / s : 0.f);
+      for (int e = 0; e < 32; ++e) {
+        const float te = fast ? quot_rn(r[k][e], s, inv) : (s > 0.f ? r[k][e] / s : 0.f);
+        t[e] = fminf(fmaxf(te, -127.0f), 127.0f);
+      }
     }
     uint32_t packed[8];
 #pragma unroll

@@ -198,6 +198,26 @@ def lora_weights(K: int, N: int, R: int, base: int = 0) -> dict:
 EMBED_V, EMBED_D, EMBED_CHUNK, EMBED_T = 248320, 4096, 8192, 32768
 
 
+def text_encoder_linear_shapes() -> list:
+    """[rows, cols] of the text encoder's 200 quantized Linear layers, a stand-in:
+    the pages give the count (200 Linear layers and the token embedding, about
+    15.9 GB in bf16) and the hidden size 4096, not the layer shapes.  The stand-in
+    follows the module list the pages name (8 full-attention layers with q/k/v/o,
+    24 linear-attention layers with in_proj_qkv, in_proj_z and out_proj -- their
+    32-output in_proj_a/b stay out of the 200 -- and 32 MLPs with gate/up/down)
+    with widths chosen so that the 200 layers hold ~6.98 G parameters, the page's
+    total less the 248320 x 4096 embedding."""
+    D, F, QKV = 4096, 12288, 8192
+    shapes = []
+    for _ in range(8):
+        shapes += [[D, D]] * 4                      # q, k, v, o
+    for _ in range(24):
+        shapes += [[QKV, D], [D, D], [D, D]]        # in_proj_qkv, in_proj_z, out_proj
+    for _ in range(32):
+        shapes += [[F, D], [F, D], [D, F]]          # gate, up, down
+    return shapes
+
+
 def embed_table(base: int = 0, V: int = EMBED_V, D: int = EMBED_D) -> np.ndarray:
     return normal_bf16((V, D), SIGMA_W, base, S_W)
 
