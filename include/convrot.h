@@ -60,6 +60,7 @@ extern "C" {
 #define CONVROT_EWORKSPACE (-3) /* workspace too small */
 #define CONVROT_EHIP (-4)       /* a HIP call or launch failed */
 #define CONVROT_EDEVICE (-5)    /* current device is not gfx950 */
+#define CONVROT_ESCRATCH (-6)   /* the call needs more than the allocation-free scratch */
 
 /* Backward modes of convrot_linear_bwd_dx. */
 #define CONVROT_BWD_BF16 0 /* transient bf16 dequantization, then a bf16 GEMM */
@@ -111,6 +112,29 @@ int convrot_quantize_weight(const uint16_t* w, int64_t rows, int64_t cols, int32
 int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw,
                        const float* sw, int64_t N, const uint16_t* bias, uint16_t* y,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Allocation-free forward, for callers that cannot allocate device memory or
+ * hand over a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same computation, kernels and result as
+ * convrot_linear_fwd (bit for bit), with q_x, s_x and any split-K partials held
+ * in a static device array of the library instead of a workspace.
+ *   - The array holds CONVROT_NOALLOC_SCRATCH_BYTES (96 MiB) on each GPU the
+ *     library runs on, from the first call on that GPU until the process ends.
+ *     A call needing more (convrot_workspace_bytes(CONVROT_OP_LINEAR_FWD, M, N,
+ *     K, 0) > CONVROT_NOALLOC_SCRATCH_BYTES; e.g. M * K above ~100 M) returns
+ *     CONVROT_ESCRATCH and enqueues nothing.
+ *   - Every call on a GPU shares that GPU's array: calls that overlap in time
+ *     on one GPU (different streams, or host threads) race and give undefined
+ *     outputs.  Calls in one stream are ordered and safe.
+ *   - The call itself allocates nothing; on the first call on a device it looks
+ *     up the array's device address (hipGetSymbolAddress) and keeps it.
+ * Other arguments, errors and ownership as convrot_linear_fwd.
+ */
+#define CONVROT_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+int convrot_linear_fwd_noalloc(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw,
+                               const float* sw, int64_t N, const uint16_t* bias, uint16_t* y,
+                               hipStream_t stream);
 
 /*
  * Forward with a LoRA branch.  The quantized layers stay LoRA-trainable and the

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(cr):
 
 
 def test_status_strings(cr):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert cr.status_string(code) != "unknown status"
     assert cr.status_string(7) == "unknown status"
 
@@ -173,6 +173,8 @@ def test_every_pointer_alignment_is_checked(cr):
                                  ["qx", "sx", "qw", "sw", "bias", "y"]),
         "convrot_linear_fwd": (["x", 64, 256, "qw", "sw", 256, "bias", "y", "ws", WS1, None],
                                ["x", "qw", "sw", "bias", "y"]),
+        "convrot_linear_fwd_noalloc": (["x", 64, 256, "qw", "sw", 256, "bias", "y", None],
+                                       ["x", "qw", "sw", "bias", "y"]),
         "convrot_linear_fwd_lora": (["x", 64, 256, "qw", "sw", 256, "bias", "a", "b", 16, 1.0, "y",
                                      "ws", WS1, None], ["x", "qw", "sw", "bias", "a", "b", "y"]),
         "convrot_lora_down": (["x", 64, 256, "a", 16, "xa", None], ["x", "a", "xa"]),
@@ -251,3 +253,23 @@ def test_activations_must_be_bf16(cr, monkeypatch):
             with pytest.raises(TypeError):
                 fn()
     assert calls == []
+
+
+def test_noalloc_forward_host_checks(cr):
+    """The allocation-free forward checks its arguments like the forward and
+    refuses, on the host and before any HIP call, a call whose q_x, s_x and
+    partials would not fit its static scratch."""
+    L = cr.lib()
+    f = L.convrot_linear_fwd_noalloc
+    assert f(None, 4, 128, B, B, 4, None, Y, None) == -1
+    assert f(A, 4, 100, B, B, 4, None, Y, None) == -2
+    assert f(None, 0, 4096, None, None, 4096, None, None, None) == 0
+    limit = cr.NOALLOC_SCRATCH_BYTES
+    # 32768 x 4096 activations need 128 MiB of codes: over the 96 MiB scratch
+    assert cr.workspace_bytes(cr.OP_LINEAR_FWD, 32768, 128, 4096) > limit
+    assert f(A, 32768, 4096, B, B, 128, None, Y, None) == -6
+    # 20480 x 4096 (the packed stream) still fits
+    assert cr.workspace_bytes(cr.OP_LINEAR_FWD, 20480, 4096, 4096) <= limit
+    m = re.search(r"#define CONVROT_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == limit

@@ -19,7 +19,8 @@ __all__ = [
     "BLOCK", "BWD_BF16", "BWD_INT8", "ConvRotError", "lib", "library_path",
     "quantize_weight", "quantize_act", "linear_fwd", "gemm_i8_bf16", "gemm_i8_i32",
     "bwd_quant_dy", "linear_bwd_dx", "dequant_weight_t", "embedding_lookup",
-    "workspace_bytes", "linear_fwd_lora", "lora_down", "EXPORTS",
+    "workspace_bytes", "linear_fwd_lora", "lora_down", "linear_fwd_noalloc",
+    "NOALLOC_SCRATCH_BYTES", "EXPORTS",
 ]
 
 BLOCK = 128
@@ -28,6 +29,7 @@ BWD_INT8 = 1
 OP_LINEAR_FWD = 0
 OP_LINEAR_BWD_DX = 1
 OP_LINEAR_FWD_LORA = 2  # mode = LoRA rank
+NOALLOC_SCRATCH_BYTES = 96 << 20  # static scratch of the allocation-free forward, per GPU
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libconvrot.so")
@@ -38,7 +40,7 @@ EXPORTS = (
     "convrot_embedding_lookup", "convrot_workspace_bytes", "convrot_status_string",
     "convrot_quantize_act", "convrot_gemm_i8_bf16", "convrot_gemm_i8_i32",
     "convrot_bwd_quant_dy", "convrot_dequant_weight_t", "convrot_linear_fwd_lora",
-    "convrot_lora_down",
+    "convrot_lora_down", "convrot_linear_fwd_noalloc",
 )
 
 
@@ -76,6 +78,7 @@ def lib():
             "convrot_linear_fwd_lora": [p, i64, i64, p, p, i64, p, p, p, i32, C.c_float, p, p,
                                         sz, p],
             "convrot_lora_down": [p, i64, i64, p, i32, p, p],
+            "convrot_linear_fwd_noalloc": [p, i64, i64, p, p, i64, p, p, p],
         }
         for name, argt in sig.items():
             f = getattr(L, name)
@@ -190,6 +193,26 @@ def linear_fwd(x, qw, sw, bias=None, out=None, workspace=None):
     ws = _ws(workspace, workspace_bytes(OP_LINEAR_FWD, M, N, K), x.device)
     _call("convrot_linear_fwd", _ptr(x), M, K, _ptr(qw), _ptr(sw), N, _ptr(bias), _ptr(y),
           _ptr(ws), ws.numel(), _stream())
+    return y
+
+
+def linear_fwd_noalloc(x, qw, sw, bias=None, out=None):
+    """The forward without a workspace: q_x, s_x and any partial sums live in the
+    library's static per-GPU scratch (NOALLOC_SCRATCH_BYTES).  Same result as
+    linear_fwd bit for bit.  Calls that overlap in time on one GPU race.  With
+    ``out`` given, the call allocates nothing."""
+    _req(x, "x", torch.bfloat16, 2)
+    _req(qw, "qw", torch.int8, 2)
+    _req(sw, "sw", torch.float32, 1)
+    M, K = x.shape
+    N = qw.shape[0]
+    _like(qw, "qw", torch.int8, (N, K))
+    _like(sw, "sw", torch.float32, (N,))
+    if bias is not None:
+        _like(bias, "bias", torch.bfloat16, (N,))
+    y = _out(out, "out", torch.bfloat16, (M, N), x.device)
+    _call("convrot_linear_fwd_noalloc", _ptr(x), M, K, _ptr(qw), _ptr(sw), N, _ptr(bias), _ptr(y),
+          _stream())
     return y
 
 

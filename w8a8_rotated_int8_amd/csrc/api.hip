@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/convrot.h"
 #include "common.h"
@@ -60,6 +61,31 @@ size_t fwd_splitk_workspace(int64_t M, int64_t N, int64_t K) {
   const int S = small_m_mode(M, N, K) ? small_m_split(M, N, K) : splitk_factor(M, N, K);
   return S > 1 ? align256((size_t)S * M * N * 4) : 0;
 }
+// The allocation-free forward's scratch: q_x, s_x and any split-K partials
+// live in this array instead of a caller workspace.  Each GPU the library runs
+// on holds its own copy until the process ends.  Host code never uses the
+// array's name as an address: the device address is looked up once per device
+// (hipGetSymbolAddress) and kept in g_scratch.
+constexpr size_t kScratchBytes = CONVROT_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch`, per device (null until looked up)
+
+int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CONVROT_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return CONVROT_EDEVICE;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CONVROT_EHIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return CONVROT_OK;
+}
+
 size_t bwd_int8_workspace(int64_t M, int64_t N) {
   return align256((size_t)M * N) + align256(4 * (size_t)M);
 }
@@ -80,6 +106,7 @@ const char* convrot_status_string(int status) {
     case CONVROT_EWORKSPACE: return "workspace too small";
     case CONVROT_EHIP: return "HIP runtime or launch error";
     case CONVROT_EDEVICE: return "current device is not gfx950";
+    case CONVROT_ESCRATCH: return "the call needs more scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }
@@ -131,15 +158,14 @@ int convrot_gemm_i8_bf16(const int8_t* qx, const float* sx, const int8_t* qw, co
   return hip_status(launch_gemm_i8(a, kEpiDequantBf16, false, stream));
 }
 
-int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw,
-                       const float* sw, int64_t N, const uint16_t* bias, uint16_t* y,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  int st = check::linear_fwd(x, M, K, qw, sw, N, bias, y, workspace);
-  if (st) return checked(st);
-  if (workspace_bytes < fwd_workspace(M, K) + fwd_splitk_workspace(M, N, K))
-    return CONVROT_EWORKSPACE;
-  st = check_device();
-  if (st) return st;
+}  // extern "C"
+
+namespace {
+
+// The forward's launches on an already validated call.
+int linear_fwd_launch(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw, const float* sw,
+                      int64_t N, const uint16_t* bias, uint16_t* y, void* workspace,
+                      hipStream_t stream) {
   int8_t* qx = static_cast<int8_t*>(workspace);
   float* sx = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + align256((size_t)M * K));
   hipError_t e = launch_rotate_quant(x, M, (int)K, qx, sx, nullptr, false, false, stream);
@@ -153,6 +179,36 @@ int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw
   const int S = splitk_factor(M, N, K);
   if (S > 1) return hip_status(launch_gemm_i8_splitk_dequant(a, S, partial, stream));
   return hip_status(launch_gemm_i8(a, kEpiDequantBf16, false, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw,
+                       const float* sw, int64_t N, const uint16_t* bias, uint16_t* y,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check::linear_fwd(x, M, K, qw, sw, N, bias, y, workspace);
+  if (st) return checked(st);
+  if (workspace_bytes < fwd_workspace(M, K) + fwd_splitk_workspace(M, N, K))
+    return CONVROT_EWORKSPACE;
+  st = check_device();
+  if (st) return st;
+  return linear_fwd_launch(x, M, K, qw, sw, N, bias, y, workspace, stream);
+}
+
+int convrot_linear_fwd_noalloc(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw,
+                               const float* sw, int64_t N, const uint16_t* bias, uint16_t* y,
+                               hipStream_t stream) {
+  int st = check::linear_fwd_noalloc(x, M, K, qw, sw, N, bias, y);
+  if (st) return checked(st);
+  if (fwd_workspace(M, K) + fwd_splitk_workspace(M, N, K) > kScratchBytes) return CONVROT_ESCRATCH;
+  st = check_device();
+  if (st) return st;
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st) return st;
+  return linear_fwd_launch(x, M, K, qw, sw, N, bias, y, ws, stream);
 }
 
 int convrot_linear_fwd_lora(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw,

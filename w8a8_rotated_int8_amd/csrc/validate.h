@@ -68,14 +68,22 @@ inline int gemm_i8_bf16(const void* qx, const void* sx, const void* qw, const vo
   return CONVROT_OK;
 }
 
-inline int linear_fwd(const void* x, int64_t M, int64_t K, const void* qw, const void* sw,
-                      int64_t N, const void* bias, const void* y, const void* workspace) {
+// The forward's tensors (convrot_linear_fwd_noalloc takes no workspace).
+inline int linear_fwd_noalloc(const void* x, int64_t M, int64_t K, const void* qw, const void* sw,
+                              int64_t N, const void* bias, const void* y) {
   if (M == 0 && N > 0 && K > 0) return row_len_ok(K) ? kNoOp : CONVROT_ESHAPE;
-  if (!x || !qw || !sw || !y || !workspace || M <= 0 || N <= 0 || K <= 0) return CONVROT_EINVAL;
-  if (!a16(x) || !a16(qw) || !a16(sw) || !a16(y) || !a16_or_null(bias) || !a256(workspace))
-    return CONVROT_EINVAL;
+  if (!x || !qw || !sw || !y || M <= 0 || N <= 0 || K <= 0) return CONVROT_EINVAL;
+  if (!a16(x) || !a16(qw) || !a16(sw) || !a16(y) || !a16_or_null(bias)) return CONVROT_EINVAL;
   if (!row_len_ok(K) || !dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N)) return CONVROT_ESHAPE;
   return CONVROT_OK;
+}
+
+// ... and with the caller's workspace (non-null, 256-byte aligned).
+inline int linear_fwd(const void* x, int64_t M, int64_t K, const void* qw, const void* sw,
+                      int64_t N, const void* bias, const void* y, const void* workspace) {
+  const bool empty = M == 0 && N > 0 && K > 0;
+  if (!empty && (!workspace || !a256(workspace))) return CONVROT_EINVAL;
+  return linear_fwd_noalloc(x, M, K, qw, sw, N, bias, y);
 }
 
 inline int linear_fwd_lora(const void* x, int64_t M, int64_t K, const void* qw, const void* sw,
