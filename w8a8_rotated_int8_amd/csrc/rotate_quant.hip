@@ -73,6 +73,164 @@ __global__ __launch_bounds__(SB == 16 ? 1024 : 512) void rotate_quant_long_kerne
                                   waves_per_row, q, scale, nullptr, row_part_max);
 }
 
+// Rows of exactly 4096 values (32 blocks; the attention and packed-stream
+// activations, most weights and the token embedding): one wave per row at a
+// time.  Lane L holds half h = L >> 5 of block b = L & 31: elements 64 h + e
+// (e < 64), 64 values in binary64.  Six butterfly stages run inside the lane
+// (element bits 0-5) and one across lanes L and L + 32 (bit 6,
+// v_permlane32_swap): half the cross-lane work of the 32-value span layout,
+// and the row maximum needs no exchange between waves.
+//
+// After the last stage lane (h, b) holds outputs 32 h + e in v[e] and
+// 64 + 32 h + e in v[e + 32] (e < 32) of block b.
+//
+// The 64 values take ~196 VGPRs, so two waves share a SIMD; to keep the SIMD
+// busy the waves are persistent and load the next row into a second LDS buffer
+// while they compute the current one.  LDS per wave: two 8 KB row buffers,
+// chunk c (16 bytes) of block b at 16 b + (c ^ (b & 7)); the current buffer
+// then stages the row's 4 KB of codes, chunk k at k ^ ((k >> 3) & 7).
+constexpr int kRow4kBlocks = 32;
+constexpr int kRow4kBytes = kRow4kBlocks * 256;
+// Below this many rows a wave gets too few rows to pipeline their loads and the
+// two-wave-per-row span kernel (four waves per SIMD) is as fast or faster
+// (same-box A/B, us: 4096 rows 13.9 vs 14.5; 20480 rows 50.2 vs 50.3; 248320
+// rows 721-726 vs 678-679).
+constexpr int64_t kRow4kMinRows = 32768;
+
+template <bool STREAM>
+__device__ __forceinline__ void stage_row4k(const uint16_t* __restrict__ x, int64_t row,
+                                            uint8_t* buf) {
+  // slot i * 64 + lane holds chunk c of block b: whole 1 KB runs of the row per
+  // load instruction
+  const int lane = threadIdx.x & 63;
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_u32(buf));
+  const uint16_t* src = x + row * (kRow4kBlocks * kBlock);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int slot = i * 64 + lane;
+    const int b = slot >> 4;
+    const int c = (slot & 15) ^ (b & 7);
+    if constexpr (STREAM) dma16_nt(src + b * kBlock + c * 8, base + i * 1024);
+    else dma16(src + b * kBlock + c * 8, base + i * 1024);
+  }
+}
+
+template <bool STREAM>
+__device__ __forceinline__ void quantize_row4k(const uint8_t* buf_in, uint8_t* buf, int64_t row,
+                                               int8_t* __restrict__ q, float* __restrict__ scale) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const int b = lane & 31;
+  const int h = lane >> 5;
+  double v[64];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 raw =
+        *reinterpret_cast<const uint4*>(buf_in + 16 * ((b << 4) | ((8 * h + i) ^ (b & 7))));
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = (double)bf16lo_to_f32(w[j]);
+      v[8 * i + 2 * j + 1] = (double)bf16hi_to_f32(w[j]);
+    }
+  }
+#pragma unroll
+  for (int bit = 1; bit < 64; bit <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 64; ++e) {
+      if (e & bit) continue;
+      const double a = v[e], c = v[e | bit];
+      v[e] = a + c;
+      v[e | bit] = a - c;
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one stage at a time (register pressure)
+  }
+  // element bit 6: lane L with L + 32
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    swap_halves(v[e], v[e + 32]);
+    const double a = v[e], c = v[e + 32];
+    v[e] = a + c;
+    v[e + 32] = a - c;
+  }
+  float r[64];
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 64; ++e) {
+    r[e] = (float)(v[e] * kInvSqrt128);
+    m = fmaxf(m, fabsf(r[e]));
+  }
+  m = max_xor32(max_xor16(group_max(m, 16)));  // the whole row: every lane
+
+  // s = fl32(m / 127), t = fl32(r / s): the 3-operation correctly rounded form
+  // for ordinary rows (m is wave-uniform, so is the branch), IEEE division with
+  // the clamp to +-127 otherwise (a subnormal s can push |t| past 127.5)
+  float s, t[64];
+  if (m >= 0x1p-64f && m <= 0x1p100f) {
+    s = quot_rn(m, 127.0f, kInv127);
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int e = 0; e < 64; ++e) t[e] = quot_rn(r[e], s, inv);
+  } else {
+    s = m / 127.0f;
+#pragma unroll
+    for (int e = 0; e < 64; ++e) t[e] = s > 0.f ? fminf(fmaxf(r[e] / s, -127.0f), 127.0f) : 0.f;
+  }
+  // codes of outputs 32 h + e (e < 32): row bytes 128 b + 32 h + e, chunks
+  // 8 b + 2 h and + 1; outputs 64 + 32 h + e: chunks 8 b + 4 + 2 h and + 1
+  auto phys = [](int k) { return k ^ ((k >> 3) & 7); };
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    uint32_t pk[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int e = 16 * grp + 4 * d;
+      pk[d] = pack_low_bytes(rne_low_byte_bits(t[e]), rne_low_byte_bits(t[e + 1]),
+                             rne_low_byte_bits(t[e + 2]), rne_low_byte_bits(t[e + 3]));
+    }
+    const int chunk = 8 * b + (grp < 2 ? 2 * h + grp : 4 + 2 * h + (grp - 2));
+    *reinterpret_cast<uint4*>(buf + 16 * phys(chunk)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staging writes landed
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+  int8_t* dst = q + row * (kRow4kBlocks * kBlock);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = 64 * j + lane;
+    const uint4 val = *reinterpret_cast<const uint4*>(buf + 16 * phys(c));
+    if constexpr (STREAM) store16_nt(dst + 16 * c, val);
+    else *reinterpret_cast<uint4*>(dst + 16 * c) = val;
+  }
+  if (lane == 0) scale[row] = s;
+}
+
+template <bool STREAM>
+__global__ __launch_bounds__(256) void rotate_quant_row4k_kernel(const uint16_t* __restrict__ x,
+                                                                 int64_t rows,
+                                                                 int8_t* __restrict__ q,
+                                                                 float* __restrict__ scale) {
+  __shared__ __align__(16) uint8_t lds[4][2][kRow4kBytes];
+  const int wave = threadIdx.x >> 6;
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= rows) return;
+  stage_row4k<STREAM>(x, row, lds[wave][0]);
+  wait_vm_n<0>();
+  for (int cur = 0;; cur ^= 1) {
+    const int64_t next = row + stride;
+    if (next < rows) stage_row4k<STREAM>(x, next, lds[wave][cur ^ 1]);
+    quantize_row4k<STREAM>(lds[wave][cur], lds[wave][cur], row, q, scale);
+    row = next;
+    if (row >= rows) break;
+    // Outstanding vector-memory operations, in issue order: this row's 8 loads
+    // (issued before the previous row's arithmetic), then the previous row's 4
+    // code stores and its scale store.  They retire in order, so once at most 5
+    // are left the row has landed in LDS.
+    wait_vm_n<5>();
+  }
+}
+
 // Fold mode, rows of at least one span (N >= 128 * kSpan): one row per
 // workgroup and no LDS staging.  Folding has no data flow between elements, so
 // lane t of the workgroup takes the 4-element units t + j * blockDim.x
@@ -199,6 +357,20 @@ hipError_t launch_rotate_quant(const uint16_t* x, int64_t rows, int K, int8_t* q
       hipLaunchKernelGGL((rotate_quant_rows_kernel<kRotate, kSpan, false>), dim3((unsigned)grid),
                          dim3(256), 4 * span_bytes<kSpan>(), stream, x, rows, K, q, scale, colscale,
                          pl.rows_per_wave);
+  } else if (K == kRow4kBlocks * kBlock && !fold && rows >= kRow4kMinRows) {
+    // persistent: two workgroups of four waves per CU (two waves per SIMD)
+    int dev = 0, n_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    int64_t grid = (rows + 3) / 4;
+    if (grid > 2 * (int64_t)n_cu) grid = 2 * (int64_t)n_cu;
+    if (weights)
+      hipLaunchKernelGGL(rotate_quant_row4k_kernel<true>, dim3((unsigned)grid), dim3(256), 0,
+                         stream, x, rows, q, scale);
+    else
+      hipLaunchKernelGGL(rotate_quant_row4k_kernel<false>, dim3((unsigned)grid), dim3(256), 0,
+                         stream, x, rows, q, scale);
   } else if (fold) {
     if (rows > 0x7fffffff) return hipErrorInvalidValue;
     const int units = K / 4;

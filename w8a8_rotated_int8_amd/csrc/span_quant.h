@@ -93,10 +93,12 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
     __builtin_amdgcn_sched_barrier(0);
     const int b = 16 * k + p;
     const bool active = b < span_blocks;
-    if (k == 1 && span_blocks <= 16) {  // wave-uniform: the span fits in one pass
+    if constexpr (NP > 1) {
+      if (k == 1 && span_blocks <= 16) {  // wave-uniform: the span fits in one pass
 #pragma unroll
-      for (int e = 0; e < 32; ++e) r[1][e] = 0.f;
-      continue;
+        for (int e = 0; e < 32; ++e) r[NP - 1][e] = 0.f;
+        continue;
+      }
     }
     uint4 raw[4];
 #pragma unroll
