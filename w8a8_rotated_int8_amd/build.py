@@ -28,6 +28,23 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+PROBE_SRC = os.path.join(HERE, "probe", "hbm_stream.hip")
+PROBE_LIB = os.path.join(HERE, "libhbm_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The streaming reference bench.py times beside the HBM-bound kernels."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [HIPCC, *FLAGS, "-I", os.path.join(HERE, "..", "include"), *sources(), "-o", tmp]
@@ -47,3 +64,4 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv))

@@ -95,7 +95,7 @@ constexpr int kRow4kBytes = kRow4kBlocks * 256;
 // two-wave-per-row span kernel (four waves per SIMD) is as fast or faster
 // (same-box A/B, us: 4096 rows 13.9 vs 14.5; 20480 rows 50.2 vs 50.3; 248320
 // rows 721-726 vs 678-679).
-constexpr int64_t kRow4kMinRows = 32768;
+constexpr int64_t kRow4kMinRows = 8192;
 
 template <bool STREAM>
 __device__ __forceinline__ void stage_row4k(const uint16_t* __restrict__ x, int64_t row,
