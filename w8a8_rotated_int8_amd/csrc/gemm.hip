@@ -300,12 +300,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
       }
     }
     const uint32_t lds_base = lds_u32(lds);
-    auto issue = [&](int kt, int buf) {
+    // The P and Q loads of stage kt into buffer buf.
+    auto issue_p = [&](int kt, int buf) {
       const int64_t kb = (int64_t)kt * BK;
       const int64_t kbp = TR ? kb * a.ldp : kb;  // P advances by rows when it is [k][i]
       const uint32_t b0 = lds_base + buf * 2 * kStage;
 #pragma unroll
-      for (int d = 0; d < 2 * kRowDma; ++d) dma16(src[d] + (d < kRowDma ? kbp : kb), b0 + dst_off[d]);
+      for (int d = 0; d < kRowDma; ++d) dma16(src[d] + kbp, b0 + dst_off[d]);
+    };
+    auto issue_q = [&](int kt, int buf) {
+      const int64_t kb = (int64_t)kt * BK;
+      const uint32_t b0 = lds_base + buf * 2 * kStage;
+#pragma unroll
+      for (int d = kRowDma; d < 2 * kRowDma; ++d) dma16(src[d] + kb, b0 + dst_off[d]);
+    };
+    auto issue = [&](int kt, int buf) {
+      issue_p(kt, buf);
+      issue_q(kt, buf);
     };
     constexpr int SL = BK / 32;
     static_assert(SL % 2 == 0, "fragment double buffer alternates per slice");
@@ -403,6 +414,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
         if (!last) {
           read_frags(buf, s + 1, F[(s + 1) & 1]);
           mfma_slice(s);
+          // the Q half of the refill started at the end of stage kt-1
+          if (s == 0 && kt >= 1 && kt - 1 + STAGES < nk) issue_q(kt - 1 + STAGES, (kt - 1) % STAGES);
         } else if constexpr (HAS_NEXT) {
           // Retire this wave's reads of stage kt, wait for stage kt+1 (at most
           // min(STAGES-2, nk-2-kt) later stages in flight) and publish; the
@@ -414,9 +427,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
           __builtin_amdgcn_sched_barrier(0);
           read_frags((kt + 1) % STAGES, 0, F[(s + 1) & 1]);
           mfma_slice(s);
-          // refill the buffer of stage kt: every wave is past its reads of it
-          // (the barrier above)
-          if (kt + STAGES < nk) issue(kt + STAGES, buf);
+          // refill the buffer of stage kt (every wave is past its reads of
+          // it: the barrier above): the P half now, the Q half after the
+          // first slice of stage kt+1.  All eight waves issuing a whole
+          // stage's loads at once right after the barrier queued 64 KB of
+          // requests together and held the waves behind them; split, the
+          // 4096^3 forward GEMM measured ~3% faster (same-box A/B, 61.8-62.5
+          // vs 60.0-60.7 us).  The wait at the end of stage kt+1 still covers
+          // both halves: with two stages it waits for every outstanding load.
+          static_assert(STAGES == 2, "the split refill assumes a two-stage ring");
+          if (kt + STAGES < nk) issue_p(kt + STAGES, buf);
         } else {
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
