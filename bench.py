@@ -30,7 +30,10 @@ rate is reported beside it.  Both are also given as a fraction of what a plain
 streaming kernel reaches for the same read/write mix on this GPU (writes stream
 markedly slower than reads), measured in the same run.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only fwd|all]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only all|fwd|kernels|copy|ceilings]
+(kernels: the hot kernels a few times each, for counter runs; copy: three 1 GiB
+device copies, the counters' calibration; ceilings: the HBM streaming rates and
+the LDS read rate per CU, as one JSON line.)
 """
 import argparse
 import hashlib
@@ -62,7 +65,7 @@ def parse():
     # insensitive to the ramp's tail.
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--only", default="all", choices=["all", "fwd", "copy", "kernels"],
+    ap.add_argument("--only", default="all", choices=["all", "fwd", "copy", "kernels", "ceilings"],
                     help="fwd: headline only; copy: a plain 1 GiB device copy (calibrates "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes); kernels: "
                          "each hot kernel a few times on its workload and the copy, for "
@@ -117,6 +120,11 @@ def main():
 
     if args.only == "kernels":
         profile_kernels(cr, torch, dev, wl, to_dev)
+        return
+
+    if args.only == "ceilings":
+        print(json.dumps({"hbm_stream_ceiling_GBps": hbm_ceiling(torch, dev),
+                          "lds_read_B_per_clk_per_cu": lds_ceiling(torch, dev)}), flush=True)
         return
 
     def time_ms(fn, warmup, iters, min_warm_s=0.08):
@@ -365,6 +373,34 @@ def hbm_ceiling(torch, dev):
         out[names[mix]] = round(best, 1)
     del src, dst
     log(f"[bench] HBM streaming ceiling (GB/s): {out}")
+    return out
+
+
+def lds_ceiling(torch, dev):
+    """LDS read rate of one CU in bytes per shader clock (libhbm_probe.so's
+    lds_probe_read: each wave streams 16-byte reads; cycles from the shader
+    cycle counter between two barriers), for 1 to 16 waves per CU, one
+    workgroup per CU.  Median over the CUs of the second of two launches."""
+    import ctypes as C
+    lib = C.CDLL(os.path.join(ROOT, "w8a8_rotated_int8_amd", "libhbm_probe.so"))
+    lib.lds_probe_read.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.lds_probe_read.restype = C.c_int
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(n_cu * 1024 * 16, dtype=torch.uint8, device=dev)
+    cyc = torch.zeros(n_cu, dtype=torch.int64, device=dev)
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    steps = 2000
+    out = {}
+    for waves in (1, 2, 4, 8, 16):
+        for _ in range(2):
+            if lib.lds_probe_read(64 * waves, steps, n_cu, C.c_void_p(sink.data_ptr()),
+                                  C.c_void_p(cyc.data_ptr()), stream) != 0:
+                raise RuntimeError("lds_probe_read failed")
+        torch.cuda.synchronize()
+        c = sorted(cyc.tolist())[n_cu // 2]
+        out[f"{waves}_waves"] = round(64 * waves * 16 * 8 * steps / c, 1)
+    del sink, cyc
+    log(f"[bench] LDS read rate per CU (B/clk): {out}")
     return out
 
 

@@ -5,7 +5,11 @@
 // datasheet peak: writes stream markedly slower than reads on this chip, so the
 // practical ceiling of a kernel depends on its read/write mix.
 //
-// Built into libhbm_probe.so by build.py; one C entry point.
+// A second probe measures the LDS read rate of one CU, in bytes per shader
+// clock, for a given number of waves each streaming 16-byte reads (the GEMM's
+// fragment reads), timed with the shader cycle counter inside the kernel.
+//
+// Built into libhbm_probe.so by build.py; two C entry points.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,9 +47,50 @@ __global__ __launch_bounds__(256) void hbm_stream_kernel(const hbm_v4u* __restri
   }
 }
 
+// Each of blockDim.x / 64 waves reads 16-byte pieces of a 64 KB LDS buffer,
+// eight independent reads per step over distinct 8 KB quarters, conflict-free
+// (lane l at +16 l).  Thread 0 records the cycles between two barriers that
+// bracket the reads.  The sink store never happens for the probe's data (the
+// xor of the reads cannot reach the constant) and keeps the reads alive.
+__global__ __launch_bounds__(1024) void lds_read_kernel(int steps, hbm_v4u* __restrict__ sink,
+                                                        unsigned long long* __restrict__ cycles) {
+  __shared__ __align__(16) hbm_v4u buf[4096];
+  for (int i = threadIdx.x; i < 4096; i += blockDim.x) buf[i] = hbm_v4u{(unsigned)i, 1u, 2u, 3u};
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  hbm_v4u acc = {0u, 0u, 0u, 0u};
+  unsigned idx = (unsigned)(wave * 64 + lane) & 4095u;
+  __syncthreads();
+  const unsigned long long t0 = __builtin_readcyclecounter();
+  for (int it = 0; it < steps; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= buf[(idx + 512u * u) & 4095u];
+    idx = (idx + 192u) & 4095u;
+  }
+  __syncthreads();
+  const unsigned long long t1 = __builtin_readcyclecounter();
+  if (acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u) sink[blockIdx.x * blockDim.x + threadIdx.x] = acc;
+  if (threadIdx.x == 0) cycles[blockIdx.x] = t1 - t0;
+}
+
 }  // namespace
 
 extern "C" {
+
+// LDS read probe: `blocks` workgroups of `threads` threads (a multiple of 64,
+// at most 1024), each wave issuing 8 * steps 16-byte reads per lane.  `sink`
+// holds blocks * threads * 16 bytes (never written in practice), `cycles`
+// blocks 64-bit counts.  Returns 0, or -1 on bad arguments / a failed launch.
+int lds_probe_read(int threads, int steps, int blocks, void* sink, void* cycles,
+                   hipStream_t stream) {
+  if (threads <= 0 || threads > 1024 || threads % 64 || steps <= 0 || blocks <= 0 || !sink || !cycles)
+    return -1;
+  if (((uintptr_t)sink & 15) || ((uintptr_t)cycles & 7)) return -1;
+  hipLaunchKernelGGL(lds_read_kernel, dim3((unsigned)blocks), dim3((unsigned)threads), 0, stream, steps,
+                     static_cast<hbm_v4u*>(sink), static_cast<unsigned long long*>(cycles));
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 
 // Stream `bytes` of output (mix 0: of input) in the given mix.  `in` must hold
 // at least: mix 0 bytes; mix 1 bytes / 2; mix 2 bytes; mix 3 2 * bytes.  `out`
