@@ -35,7 +35,9 @@
  *   the rotated values; the rotation sum is carried out exactly (fp64) and the
  *   product with the constant is rounded to fp64 then to fp32; a row whose
  *   scale is 0 (all zero, or a maximum so small that a / 127 underflows) has
- *   codes 0.
+ *   codes 0; a row with a NaN or infinite value r (a non-finite input, or an
+ *   fp32 overflow of the rotated value) has scale NaN (the canonical quiet NaN,
+ *   bits 0x7fc00000) and codes 0, so that it dequantizes to NaN.
  *
  * Floating-point environment: built with -O2 -fno-fast-math -ffp-contract=off,
  * so every expression below rounds exactly as written.
@@ -179,9 +181,19 @@ int oracle_rotate_rows(const uint16_t* x, int64_t rows, int64_t cols, int block,
 
 static void quantize_one_row(const float* r, int64_t cols, int8_t* q, float* s_out) {
     float a = 0.0f;
+    int finite = 1;
     for (int64_t j = 0; j < cols; ++j) {
         float v = fabsf(r[j]);
-        if (v > a) a = v;
+        if (!isfinite(v)) finite = 0;
+        else if (v > a) a = v;
+    }
+    /* A NaN or infinite r has no finite scale: the row gets the canonical quiet
+     * NaN as its scale and codes 0, and dequantizes to NaN. */
+    if (!finite) {
+        const uint32_t nan_bits = 0x7fc00000u;
+        memcpy(s_out, &nan_bits, sizeof nan_bits);
+        for (int64_t j = 0; j < cols; ++j) q[j] = 0;
+        return;
     }
     float s = a / 127.0f; /* IEEE binary32 division */
     /* A zero scale dequantizes every code to 0 and leaves r / s undefined: the

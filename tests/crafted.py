@@ -28,3 +28,45 @@ def tiny_fold_rows(N: int, seed: int = 0):
     for e in (-124, -125, -127):
         rows.append(g.uniform(-1, 1, N).astype(np.float32) * np.float32(2.0 ** e))
     return wl.f32_to_bf16_bits(np.stack(rows)), np.full(N, 2.0 ** -20, np.float32)
+
+
+BF16_NAN, BF16_INF, BF16_NINF, BF16_MAX = 0x7FC0, 0x7F80, 0xFF80, 0x7F7F
+
+
+def nonfinite_rows(K: int, seed: int = 0):
+    """bf16 rows (K a multiple of 128) that are not finite after the rotation,
+    each among ordinary N(0, 1) values, followed by one ordinary row:
+      * a NaN input in the last block;
+      * +inf in the first block; -inf in the middle;
+      * +inf and -inf in one block (its sums are NaN);
+      * a whole block of bf16's largest finite value (3.39e38): its rotated sum
+        128 * 3.39e38 / sqrt(128) overflows fp32 to +inf;
+      * every element NaN."""
+    g = np.random.default_rng(seed)
+    base = wl.f32_to_bf16_bits(g.standard_normal((7, K)).astype(np.float32))
+    rows = base.copy()
+    rows[0, K - 5] = BF16_NAN
+    rows[1, 3] = BF16_INF
+    rows[2, K // 2 + 7] = BF16_NINF
+    rows[3, 10] = BF16_INF
+    rows[3, 100] = BF16_NINF
+    rows[4, 128:256 if K >= 256 else 128] = BF16_MAX
+    if K < 256:
+        rows[4, :128] = BF16_MAX
+    rows[5, :] = BF16_NAN
+    return rows  # row 6 stays ordinary
+
+
+def nonfinite_fold_rows(N: int, seed: int = 0):
+    """dY rows and column scales whose fold r = fl32(dY) * s_w is not finite in
+    some column (NaN, +-inf inputs; a finite 2^100 times a column scale of 2^40,
+    which overflows fp32), followed by one ordinary row."""
+    g = np.random.default_rng(seed)
+    dy = wl.f32_to_bf16_bits(g.standard_normal((5, N)).astype(np.float32))
+    sw = np.full(N, 2.0 ** -3, np.float32)
+    dy[0, N - 1] = BF16_NAN
+    dy[1, 0] = BF16_INF
+    dy[2, N // 3] = BF16_NINF
+    dy[3, 7] = wl.f32_to_bf16_bits(np.float32([2.0 ** 100]))[0]
+    sw[7] = np.float32(2.0 ** 40)
+    return dy, sw  # row 4 stays ordinary (its column 7 folds to a finite value)

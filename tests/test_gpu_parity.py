@@ -32,7 +32,7 @@ def orc():
     return oracle
 
 
-from crafted import tiny_fold_rows  # noqa: E402
+from crafted import nonfinite_fold_rows, nonfinite_rows, tiny_fold_rows  # noqa: E402
 from gpu_util import (Guarded, assert_exact, assert_fwd_elementwise, assert_rows_close,  # noqa: E402
                       bf16_to_dev, bits, guarded_workspace, host, to_dev)
 
@@ -83,6 +83,73 @@ def test_quantize_act_exact(cr, orc, M, K):
     assert bad == 0
     assert_exact(host(s), os_, "scales")
     assert_exact(host(q), oq, "codes")
+
+
+NAN_BITS = 0x7FC00000
+
+
+@pytest.mark.parametrize("K", [128, 256, 4096, 4224, 16384])
+def test_quantize_nonfinite_rows(cr, orc, K):
+    # rows with a NaN or infinite rotated value (non-finite inputs, an inf - inf
+    # block, an fp32 overflow of the rotation): NaN scale and zero codes on
+    # every quantizer path, bit for bit with the oracle; ordinary rows around
+    # them are unaffected (short rows share a wave with their neighbours)
+    say(f"quantize nonfinite rows K={K}")
+    x = np.concatenate([wl.activations(37, K, max(1, wl.n_outliers(K)), base=K),
+                        nonfinite_rows(K, K), wl.activations(5, K, 1, base=K + 1)])
+    oq, os_, _ = orc.rotate_quantize(x)
+    assert (os_[37:43].view(np.uint32) == NAN_BITS).all() and not oq[37:43].any()
+    for name, fn in (("act", cr.quantize_act), ("weight", cr.quantize_weight)):
+        q, s = fn(bf16_to_dev(x))
+        assert_exact(host(s), os_, f"{name} scales")
+        assert_exact(host(q), oq, f"{name} codes")
+
+
+def test_quantize_nonfinite_rows_row_kernel(cr, orc):
+    # the 4096-wide row kernel (8192 rows and more, activations and chunked
+    # weights): crafted rows at the start, middle and end of the batch
+    say("quantize nonfinite rows, 8192 x 4096 row kernel")
+    K, M = 4096, 8192
+    x = np.zeros((M, K), np.uint16)
+    bad = nonfinite_rows(K, 3)
+    picks = [0, 1, 4095, 4096, M - 8, M - 1]
+    for i, r in enumerate(picks):
+        x[r] = bad[i % bad.shape[0]]
+    x[100] = bad[6]  # an ordinary row
+    rows = picks + [100]
+    oq, os_, _ = orc.rotate_quantize(x[rows])
+    for name, fn in (("act", lambda t: cr.quantize_act(t)),
+                     ("weight", lambda t: cr.quantize_weight(t, chunk_rows=M))):
+        q, s = fn(bf16_to_dev(x))
+        assert_exact(host(s)[rows], os_, f"{name} scales")
+        assert_exact(host(q)[rows], oq, f"{name} codes")
+
+
+@pytest.mark.parametrize("N", [256, 2048, 4224])
+def test_bwd_quant_dy_nonfinite_rows(cr, orc, N):
+    say(f"bwd_quant_dy nonfinite rows N={N}")
+    dy, sw = nonfinite_fold_rows(N, N)
+    qg, sg = cr.bwd_quant_dy(bf16_to_dev(dy), torch.from_numpy(sw).cuda())
+    oqg, osg = orc.bwd_quant_dy(dy, sw)
+    assert (osg[:4].view(np.uint32) == NAN_BITS).all() and np.isfinite(osg[4])
+    assert_exact(host(sg), osg, "s_g")
+    assert_exact(host(qg), oqg, "q_g")
+
+
+def test_forward_nonfinite_row_gives_nan_output_row(cr):
+    # a NaN activation row comes out of the forward as a NaN output row; the
+    # other rows are the same as without it
+    say("forward with a nonfinite activation row")
+    t = wl.tiny(0)
+    x = t["x"].copy()
+    x[3, 17] = 0x7FC0
+    qw, sw = cr.quantize_weight(bf16_to_dev(t["w"]))
+    y = bits(cr.linear_fwd(bf16_to_dev(x), qw, sw))
+    y0 = bits(cr.linear_fwd(bf16_to_dev(t["x"]), qw, sw))
+    yf = wl.bf16_bits_to_f32(y)
+    assert np.isnan(yf[3]).all()
+    keep = np.arange(x.shape[0]) != 3
+    assert np.array_equal(y[keep], y0[keep])
 
 
 def test_quantize_weight_tiny_and_chunked(cr, orc):

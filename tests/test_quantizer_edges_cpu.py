@@ -28,7 +28,7 @@ import numpy as np
 import pytest
 
 import workloads as wl
-from crafted import tiny_fold_rows
+from crafted import nonfinite_fold_rows, nonfinite_rows, tiny_fold_rows
 
 pytestmark = pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
 
@@ -103,20 +103,23 @@ static int8_t low_byte(float t) {
 }
 
 /* The fold quantizer of the int8 input gradient, as the kernels evaluate it:
-   r = fl32(dY) * s_w; m = max |r|; ordinary rows (m in [2^-64, 2^100]) take
-   s = quot_rn(m, 127, RN(1/127)) and t = quot_rn(r, s, RN(1/s)); other rows take
-   the IEEE divisions, t clamped to [-127, 127] when clamp != 0, codes 0 when
-   s == 0. */
+   r = fl32(dY) * s_w; m = max |r| under the NaN-propagating maximum; ordinary
+   rows (m in [2^-64, 2^100]) take s = quot_rn(m, 127, RN(1/127)) and
+   t = quot_rn(r, s, RN(1/s)); other rows take the IEEE divisions, t clamped to
+   [-127, 127] when clamp != 0, codes 0 when s == 0; a non-finite m gives the
+   canonical NaN scale (and, since s > 0 fails, codes 0). */
+static float max_nan(float a, float b) { return (isnan(a) || isnan(b)) ? NAN : fmaxf(a, b); }
+static float nan_scale(void) { uint32_t u = 0x7fc00000u; float f; memcpy(&f, &u, 4); return f; }
 void emu_fold(const uint16_t* dy, int64_t M, int64_t N, const float* sw, int clamp,
               int8_t* q, float* s_out) {
   const float y127 = 0x1.020408p-7f;
   for (int64_t m = 0; m < M; ++m) {
     float mx = 0.f;
-    for (int64_t n = 0; n < N; ++n) mx = fmaxf(mx, fabsf(bf16f(dy[m * N + n]) * sw[n]));
+    for (int64_t n = 0; n < N; ++n) mx = max_nan(mx, fabsf(bf16f(dy[m * N + n]) * sw[n]));
     float s;
     int fast = mx >= 0x1p-64f && mx <= 0x1p100f;
     if (fast) s = quot_rn(mx, 127.0f, y127);
-    else s = mx / 127.0f;
+    else s = mx <= 0x1.fffffep127f ? mx / 127.0f : nan_scale();
     float inv = s > 0.f ? 1.0f / s : 0.f;
     for (int64_t n = 0; n < N; ++n) {
       float r = bf16f(dy[m * N + n]) * sw[n], t;
@@ -205,6 +208,60 @@ def test_kernel_branches_match_the_oracle_on_ordinary_rows(oracle_mod, emu):
     q, s = emu_fold(emu, dy, sw)
     assert np.array_equal(s.view(np.uint32), os_.view(np.uint32))
     assert np.array_equal(q, oq)
+
+
+def test_kernel_branches_match_the_oracle_on_nonfinite_rows(oracle_mod, emu):
+    # a NaN or infinite fold: the NaN-propagating maximum sends the row to the
+    # NaN scale with codes 0 in the emulated kernel and in the oracle alike
+    dy, sw = nonfinite_fold_rows(1152, 4)
+    oq, os_ = oracle_mod.bwd_quant_dy(dy, sw)
+    q, s = emu_fold(emu, dy, sw)
+    assert np.array_equal(s.view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(q, oq)
+    assert (os_[:4].view(np.uint32) == NAN_BITS).all() and not oq[:4].any()
+    assert np.isfinite(os_[4]) and os_[4] > 0
+
+
+# --------------------------------------------------------------------------
+# Non-finite rows (oracle pins)
+# --------------------------------------------------------------------------
+
+NAN_BITS = 0x7FC00000
+
+
+def test_nonfinite_values_give_the_nan_scale(oracle_mod):
+    # NaN, +inf, -inf anywhere in a row: scale = the canonical quiet NaN, codes
+    # 0 (the row dequantizes to NaN); a finite row in the same call is untouched
+    r = f32([[1.0, np.nan, -2.0, 0.5], [1.0, np.inf, -2.0, 0.5], [-np.inf, 3.0, 0.0, 1.0],
+             [1.0, 4.0, -2.0, 0.5]])
+    q, s = oracle_mod.quantize_rows(r)
+    assert (s[:3].view(np.uint32) == NAN_BITS).all()
+    assert not q[:3].any()
+    q3, s3 = oracle_mod.quantize_rows(r[3:])
+    assert s[3] == s3[0] and np.array_equal(q[3], q3[0]) and q3[0, 1] == 127
+
+
+def test_rotation_of_nonfinite_rows(oracle_mod):
+    # every crafted row is non-finite after the rotation (a NaN, +-inf, an
+    # inf - inf block, an fp32 overflow of a block of bf16's largest value);
+    # the last row is ordinary and keeps a finite scale
+    for K in (128, 256, 4096):
+        x = nonfinite_rows(K, K)
+        q, s, _ = oracle_mod.rotate_quantize(x)
+        assert (s[:6].view(np.uint32) == NAN_BITS).all(), K
+        assert not q[:6].any(), K
+        assert np.isfinite(s[6]) and s[6] > 0, K
+
+
+def test_rotated_overflow_is_nonfinite(oracle_mod):
+    # a block of 128 copies of bf16's largest value v: the rotated DC value is
+    # fl32(128 v / sqrt(128)) = fl32(11.3 v) = +inf; the other 127 are 0
+    v = 0x7F7F
+    x = np.full((1, 128), v, np.uint16)
+    r, _ = oracle_mod.rotate_rows(x)
+    assert np.isinf(r[0, 0]) and not r[0, 1:].any()
+    q, s, _ = oracle_mod.rotate_quantize(x)
+    assert s.view(np.uint32)[0] == NAN_BITS and not q.any()
 
 
 # --------------------------------------------------------------------------

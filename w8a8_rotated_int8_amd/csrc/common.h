@@ -106,10 +106,22 @@ __device__ __forceinline__ void swap_halves(float& vdst, float& src0) {
   src0 = __uint_as_float(b);
 }
 
-// Cross-lane maxima of non-negative, non-NaN floats (row maxima of |r| that
-// start from +0 under fmaxf, which drops NaN): on such values the order of the
-// bit patterns as unsigned integers is the order of the floats, so the lanes
-// combine with integer max and no NaN canonicalisation is needed.
+// Row maxima of |r|.  Every quantizer takes them with the IEEE 754-2019
+// maximum, which returns NaN when either operand is NaN (v_maximum3_f32 on
+// gfx950, at the cost of the NaN-dropping v_max3_f32): a NaN or infinite
+// rotated value then makes the row's maximum non-finite, and the quantizers
+// give such a row a NaN scale and zero codes instead of silently dropping it.
+__device__ __forceinline__ float max_nan(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+// The quantizers' NaN scale: the canonical quiet NaN, so that the scale of a
+// non-finite row has one bit pattern on every path.
+constexpr uint32_t kScaleNaNBits = 0x7fc00000u;
+
+// Cross-lane maxima of non-negative floats, NaN included (row maxima of |r|,
+// from +0 under max_nan): on such values the order of the bit patterns as
+// unsigned integers is the order of the floats, and a positive NaN's bits lie
+// above +inf's, so the lanes combine with integer max and a NaN survives.
 //
 // DPP lane patterns within each 16-lane row (gfx9 dpp_ctrl encodings).
 constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]: lane i <- i ^ 1

@@ -158,13 +158,14 @@ __device__ __forceinline__ void quantize_row4k(const uint8_t* buf_in, uint8_t* b
 #pragma unroll
   for (int e = 0; e < 64; ++e) {
     r[e] = (float)(v[e] * kInvSqrt128);
-    m = fmaxf(m, fabsf(r[e]));
+    m = max_nan(m, fabsf(r[e]));
   }
   m = max_xor32(max_xor16(group_max(m, 16)));  // the whole row: every lane
 
   // s = fl32(m / 127), t = fl32(r / s): the 3-operation correctly rounded form
   // for ordinary rows (m is wave-uniform, so is the branch), IEEE division with
-  // the clamp to +-127 otherwise (a subnormal s can push |t| past 127.5)
+  // the clamp to +-127 otherwise (a subnormal s can push |t| past 127.5), and
+  // the NaN scale with codes 0 for a non-finite maximum
   float s, t[64];
   if (m >= 0x1p-64f && m <= 0x1p100f) {
     s = quot_rn(m, 127.0f, kInv127);
@@ -172,7 +173,8 @@ __device__ __forceinline__ void quantize_row4k(const uint8_t* buf_in, uint8_t* b
 #pragma unroll
     for (int e = 0; e < 64; ++e) t[e] = quot_rn(r[e], s, inv);
   } else {
-    s = m / 127.0f;
+    // a non-finite maximum gives the NaN scale, and s > 0 fails: codes 0
+    s = m <= 0x1.fffffep127f ? m / 127.0f : __uint_as_float(kScaleNaNBits);
 #pragma unroll
     for (int e = 0; e < 64; ++e) t[e] = s > 0.f ? fminf(fmaxf(r[e] / s, -127.0f), 127.0f) : 0.f;
   }
@@ -268,13 +270,13 @@ __global__ __launch_bounds__(1024) void fold_quant_rows_kernel(
     r[j][2] = bf16lo_to_f32(raw[j].y) * sc[j].z;
     r[j][3] = bf16hi_to_f32(raw[j].y) * sc[j].w;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(r[j][e]));
+    for (int e = 0; e < 4; ++e) m = max_nan(m, fabsf(r[j][e]));
   }
   m = max_xor32(max_xor16(group_max(m, 16)));
   if (lane == 0) part[wave] = m;
   __syncthreads();
   m = 0.f;
-  for (int w = 0; w < nwaves; ++w) m = fmaxf(m, part[w]);
+  for (int w = 0; w < nwaves; ++w) m = max_nan(m, part[w]);
 
   // m is the same in every lane, so both branches are workgroup-uniform.
   float s, t[kFoldUnits][4];
@@ -289,8 +291,9 @@ __global__ __launch_bounds__(1024) void fold_quant_rows_kernel(
     // Extreme rows: IEEE division.  When s is subnormal its rounding error can
     // push |t| past 127.5 (a folded maximum of 2^-140 gives s = 2^-147 and
     // t = 128), so the codes are clamped to [-127, 127]; a zero s (a/127
-    // underflowed) gives codes 0.
-    s = m / 127.0f;
+    // underflowed) gives codes 0, and so does the NaN scale of a non-finite
+    // maximum.
+    s = m <= 0x1.fffffep127f ? m / 127.0f : __uint_as_float(kScaleNaNBits);
 #pragma unroll
     for (int j = 0; j < kFoldUnits; ++j)
 #pragma unroll

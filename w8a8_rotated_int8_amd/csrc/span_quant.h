@@ -14,7 +14,9 @@
 //             checks those rows against the index-order sum).
 //   fold:     (dY quantizer) r_n = fl32(fl32(dY_n) * s_w[n]); no rotation.
 //   quantize: a = max|r|, s = fl32(a/127), code = clamp(RNE(fl32(r/s)), +-127);
-//             s = 0 (all-zero row, or a/127 underflowed) -> codes 0.
+//             s = 0 (all-zero row, or a/127 underflowed) -> codes 0; a row with
+//             a NaN or infinite r (non-finite input, or fl32 overflow of the
+//             rotation) -> s = NaN (canonical quiet NaN) and codes 0.
 //
 // Work layout.  A wave owns a span of SB blocks: several short rows packed
 // together, or an SB-block slice of a longer row (then the workgroup's waves
@@ -180,12 +182,12 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
   for (int k = 0; k < NP; ++k) {
     m[k] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) m[k] = fmaxf(m[k], fabsf(r[k][e]));
+    for (int e = 0; e < 32; ++e) m[k] = max_nan(m[k], fabsf(r[k][e]));
     m[k] = max_xor32(max_xor16(m[k]));  // the four quarters of the block
   }
   float mall = m[0];
 #pragma unroll
-  for (int k = 1; k < NP; ++k) mall = fmaxf(mall, m[k]);
+  for (int k = 1; k < NP; ++k) mall = max_nan(mall, m[k]);
   if (waves_per_row == 1) {
     if (nb == SB) {
       const float mm = group_max(mall, 16);
@@ -207,7 +209,7 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
         float mm = 0.f;
         for (int j = 0; j < nb; ++j) {
           const int idx = first + j;
-          if (idx < SB) mm = fmaxf(mm, seg_max_wave[idx]);
+          if (idx < SB) mm = max_nan(mm, seg_max_wave[idx]);
         }
         m[k] = mm;
       }
@@ -217,7 +219,7 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
     if (lane == 0) row_part_max[wave] = mw;
     __syncthreads();
     float mm = 0.f;
-    for (int w = 0; w < waves_per_row; ++w) mm = fmaxf(mm, row_part_max[w]);
+    for (int w = 0; w < waves_per_row; ++w) mm = max_nan(mm, row_part_max[w]);
 #pragma unroll
     for (int k = 0; k < NP; ++k) m[k] = mm;
   }
@@ -244,7 +246,9 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
 #pragma unroll
       for (int e = 0; e < 32; ++e) t[e] = quot_rn(r[k][e], s, inv);
     } else {
-      s = m[k] / 127.0f;                               // IEEE binary32 division
+      // IEEE binary32 division; a non-finite maximum (a NaN or infinite
+      // rotated value in the row) gives the NaN scale, whose codes are 0
+      s = m[k] <= 0x1.fffffep127f ? m[k] / 127.0f : __uint_as_float(kScaleNaNBits);
       const float inv = s > 0.f ? 1.0f / s : 0.f;
       // A subnormal s carries a relative rounding error that can push |t| past
       // 127.5 (e.g. a = 2^-140: s = 2^-147, t = 128), so the codes are clamped
