@@ -261,15 +261,15 @@ def source_hash(files):
     return h.hexdigest()
 
 
-def counter_traffic(record, sources):
-    """HBM bytes per launch from a committed rocprofv3 counter summary
-    (profiles/<record>), if it was taken on the current source of the kernel;
-    else None."""
+def counter_traffic(record, sources, key="hbm_bytes_per_launch"):
+    """HBM bytes (per launch, or the record's other `key`) from a committed
+    rocprofv3 counter summary (profiles/<record>), if it was taken on the
+    current source of the kernel; else None."""
     p = os.path.join(ROOT, "profiles", record)
     try:
         rec = json.load(open(p))
         if rec.get("source_sha256") == source_hash(sources):
-            return rec.get("hbm_bytes_per_launch")
+            return rec.get(key)
     except (OSError, ValueError):
         pass
     return None
@@ -531,8 +531,10 @@ def bench_embedding(cr, torch, dev, dev_normal, time_ms, wl):
         "embed_quant_us": round(q_ms * 1e3, 1),
         "embed_quant_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
         "embed_quant_pct_hbm": round(100 * q_bytes / (q_ms * 1e-3) / 1e9 / 8000.0, 1),
+        # per quantization of the whole table (31 chunk launches)
         "embed_quant_traffic_bytes": counter_traffic("rotate_quant_embed_pmc.json",
-                                                     ["rotate_quant.hip", "span_quant.h", "common.h"]),
+                                                     ["rotate_quant.hip", "span_quant.h", "common.h"],
+                                                     "hbm_bytes_per_call"),
         "embed_lookup_from_hbm_us": round(lc_ms * 1e3, 1),
         "embed_lookup_from_hbm_GBps": round(l_bytes / (lc_ms * 1e-3) / 1e9, 1),
         "embed_lookup_from_hbm_pct_hbm": round(100 * l_bytes / (lc_ms * 1e-3) / 1e9 / 8000.0, 1),
