@@ -82,7 +82,11 @@ extern "C" {
  * while a 128-block's magnitude spread stays under about 2^38),
  * a = max |r|, scale = fl32(a / 127), codes = round-half-even(fl32(r / scale))
  * clamped to [-127, 127].  A row whose scale is 0 (all zero, or a maximum below
- * 127 * 2^-150, where a / 127 underflows) gets codes 0.
+ * 127 * 2^-150, where a / 127 underflows) gets codes 0.  A row with a NaN or
+ * infinite r (a non-finite input, or an fp32 overflow of the rotated value) gets
+ * scale NaN (0x7fc00000) and codes 0, so it dequantizes to NaN; the forward's
+ * activation quantizer and the int8 input gradient's dY quantizer apply the
+ * same rules per row.
  *   w      bf16 [rows, cols], cols % 128 == 0, cols <= CONVROT_MAX_ROW_LEN
  *   block  must be 128
  *   chunk_rows  rows per launch (0 = all rows at once); results do not depend on it
