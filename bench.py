@@ -32,8 +32,8 @@ markedly slower than reads), measured in the same run.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only all|fwd|kernels|copy|ceilings]
 (kernels: the hot kernels a few times each, for counter runs; copy: three 1 GiB
-device copies, the counters' calibration; ceilings: the HBM streaming rates and
-the LDS read rate per CU, as one JSON line.)
+device copies, the counters' calibration; ceilings: the HBM streaming rates, the
+LDS read rate per CU and the sustained int8 / bf16 MFMA rates, as one JSON line.)
 """
 import argparse
 import hashlib
@@ -124,7 +124,8 @@ def main():
 
     if args.only == "ceilings":
         print(json.dumps({"hbm_stream_ceiling_GBps": hbm_ceiling(torch, dev),
-                          "lds_read_B_per_clk_per_cu": lds_ceiling(torch, dev)}), flush=True)
+                          "lds_read_B_per_clk_per_cu": lds_ceiling(torch, dev),
+                          "mfma_sustained": mfma_ceiling(torch, dev)}), flush=True)
         return
 
     def time_ms(fn, warmup, iters, min_warm_s=0.08):
@@ -208,6 +209,13 @@ def main():
         "act_quant_us": round(aq_ms * 1e3, 2),
         "act_quant_GBps_mall_resident": round(aq_bytes / (aq_ms * 1e-3) / 1e9, 1),
     }
+    # the same GEMM and call against the matrix cores' sustained rate on this
+    # chip (register operands, no memory traffic), beside the datasheet peak
+    mc = mfma_ceiling(torch, dev)
+    extra["mfma_sustained"] = mc
+    for d in ("codes", "random"):
+        extra[f"gemm_pct_of_sustained_int8_{d}"] = round(100 * gemm_tops / mc[f"int8_{d}_TOPS"], 1)
+        extra[f"linear_fwd_pct_of_sustained_int8_{d}"] = round(100 * tops / mc[f"int8_{d}_TOPS"], 1)
     wq_ms = time_ms(lambda: cr.quantize_weight(w, out=(qw, sw)), 3, 20)
     extra["weight_quant_attn_us"] = round(wq_ms * 1e3, 2)
     # the same forward with a rank-16 LoRA branch on the unrotated input
@@ -229,6 +237,9 @@ def main():
         extra.update(bench_small_m(cr, torch, dev, dev_normal, time_ms, wl))
         extra.update(bench_embedding(cr, torch, dev, dev_normal, time_ms, wl))
         extra.update(bench_mlp(cr, torch, dev, dev_normal, time_ms, wl))
+        for k in ("mlp_down_dx_bf16_tops", "mlp_up_dx_bf16_tops"):
+            extra[k.replace("_tops", "_pct_of_sustained_bf16")] = round(
+                100 * extra[k] / mc["bf16_random_TFLOPS"], 1)
         extra.update(bench_packed(cr, torch, dev, dev_normal, time_ms, wl))
         extra.update(bench_text_encoder_quant(cr, torch, dev, dev_normal, wl))
         extra.update(bench_vendor_int8(torch, dev, time_ms, extra.get("gemm_kernel_us")))
@@ -401,6 +412,62 @@ def lds_ceiling(torch, dev):
         out[f"{waves}_waves"] = round(64 * waves * 16 * 8 * steps / c, 1)
     del sink, cyc
     log(f"[bench] LDS read rate per CU (B/clk): {out}")
+    return out
+
+
+def mfma_ceiling(torch, dev):
+    """Sustained matrix-core rate (libhbm_probe.so's mfma_probe_run): every
+    SIMD issues back-to-back independent MFMAs on register operands, four waves
+    per SIMD, no memory traffic, ~10 ms per launch after at least 200 ms of the
+    same load.  The chip lowers its clock to stay within its power limit, and
+    how far depends on how many operand bits switch, so the int8 form runs with
+    random bytes, with code-like bytes (the spread of per-row int8 codes) and
+    with zero operands (no switching: the datasheet rate at full clock); the
+    bf16 form with random mantissas.  Median of five timed launches; the clock
+    is the median over workgroups of shader cycles against the 100 MHz
+    real-time counter."""
+    import ctypes as C
+    lib = C.CDLL(os.path.join(ROOT, "w8a8_rotated_int8_amd", "libhbm_probe.so"))
+    lib.mfma_probe_run.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
+                                   C.c_void_p]
+    lib.mfma_probe_run.restype = C.c_int
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks, threads, steps = 2 * n_cu, 512, 20000
+    sink = torch.empty(blocks * threads * 64, dtype=torch.uint8, device=dev)
+    stamps = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def launch(kind):
+        if lib.mfma_probe_run(kind, threads, steps, blocks, C.c_void_p(sink.data_ptr()),
+                              C.c_void_p(stamps.data_ptr()), stream) != 0:
+            raise RuntimeError("mfma_probe_run failed")
+
+    out = {}
+    for kind, name, ops_each, unit in ((0, "int8_random", 65536, "TOPS"),
+                                       (1, "int8_codes", 65536, "TOPS"),
+                                       (2, "int8_zero", 65536, "TOPS"),
+                                       (3, "bf16_random", 32768, "TFLOPS")):
+        t_end = time.perf_counter() + 0.2
+        while time.perf_counter() < t_end:
+            launch(kind)
+            torch.cuda.synchronize()
+        ts, clocks = [], []
+        for _ in range(5):
+            e0.record()
+            launch(kind)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+            st = stamps.view(blocks, 2).tolist()
+            ghz = sorted(c / (r / 100e6) / 1e9 for c, r in st if r > 0)
+            clocks.append(ghz[len(ghz) // 2])
+        ms = sorted(ts)[2]
+        ops = blocks * (threads // 64) * steps * 8 * ops_each
+        out[f"{name}_{unit}"] = round(ops / (ms * 1e-3) / 1e12, 1)
+        out[f"{name}_GHz"] = round(sorted(clocks)[2], 3)
+    del sink, stamps
+    log(f"[bench] sustained MFMA rate, register operands: {out}")
     return out
 
 
