@@ -25,8 +25,8 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-from gpu_util import (Guarded, assert_exact, assert_fwd_elementwise, assert_rows_close,  # noqa: E402
-                      bf16_to_dev, bits, guarded_workspace, host)
+from gpu_util import (CANARY, Guarded, assert_exact, assert_fwd_elementwise,  # noqa: E402
+                      assert_rows_close, bf16_to_dev, bits, guarded_workspace, host)
 
 
 @pytest.fixture(scope="module")
@@ -98,3 +98,72 @@ def test_small_m_with_bias(cr, M, K, N):
     y = cr.linear_fwd(xd, qw, sw, bias=bias)
     qx, sx = cr.quantize_act(xd)
     assert torch.equal(y, cr.gemm_i8_bf16(qx, sx, qw, sw, bias=bias))
+
+
+# The one-launch forward of very few rows: every workgroup rotates and
+# quantizes x's rows itself, in LDS, and runs the few-row contraction (at most
+# 8 / ceil(K / 2048) rows).  Shapes: one wave per row (K <= 2048; power-of-two
+# and other block counts, up to 8 rows), two (K = 4096, up to 4 rows), three
+# (K = 4224 and 6144: 2 rows, two waves without a row) and four (K = 8192, 2
+# rows); ragged and skinny N.
+FUSED = [(1, 128, 4096), (8, 128, 40), (3, 384, 1000), (8, 1152, 4096), (5, 2048, 2000),
+         (8, 2048, 16), (1, 4096, 4096), (2, 4096, 4096), (4, 4096, 4096), (3, 4096, 8192),
+         (1, 4224, 4096), (2, 6144, 1000), (2, 8192, 4096), (1, 8192, 8)]
+
+
+@pytest.mark.parametrize("with_bias", [False, True])
+@pytest.mark.parametrize("M,K,N", FUSED)
+def test_fused_few_row_forward(cr, M, K, N, with_bias):
+    import oracle
+    print(f"fused forward M={M} K={K} N={N} bias={with_bias}", flush=True)
+    x = wl.activations(M, K, wl.n_outliers(K), base=2)
+    w = wl.packed_weight(4200 + N % 997, 2, N, K)
+    bias_np = wl.normal_bf16((N,), 1.0, 2, 19) if with_bias else None
+    bias = bf16_to_dev(bias_np) if with_bias else None
+    qw, sw = cr.quantize_weight(bf16_to_dev(w))
+    xd = bf16_to_dev(x)
+    gy = Guarded((M, N), torch.bfloat16)
+    gws = guarded_workspace(cr.workspace_bytes(cr.OP_LINEAR_FWD, M, N, K))
+    y = cr.linear_fwd(xd, qw, sw, bias=bias, out=gy.t, workspace=gws.t)
+    gy.check("y")
+    gws.check("workspace")
+    # q_x and s_x never leave LDS: the workspace still holds the canary (the
+    # two-launch forward writes q_x there), so this is the one-launch path
+    assert bool((gws.t == CANARY).all()), "the workspace was written: not the one-launch forward"
+    qx, sx = cr.quantize_act(xd)
+    y1 = cr.gemm_i8_bf16(qx, sx, qw, sw, bias=bias)
+    assert np.array_equal(bits(y), bits(y1)), "one-launch forward differs from the two launches"
+    oqx, osx, _ = oracle.rotate_quantize(x)
+    oqw, osw, _ = oracle.rotate_quantize(w)
+    assert_exact(host(qx), oqx, "q_x")
+    oy = oracle.dequant_epilogue(oracle.gemm_i8_i32(oqx, oqw), osx, osw, bias=bias_np)
+    e = assert_rows_close(bits(y), oy, "y")
+    if not with_bias:  # the one-ulp bound is for the product alone (a bias can cancel it)
+        assert_fwd_elementwise(bits(y), oy, "y")
+    print(f"  max row relerr {e:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("M,K", [(2, 4096), (8, 1024), (2, 8192)])
+def test_fused_few_row_forward_nonfinite_row(cr, M, K):
+    # a NaN or infinite activation gives its row the NaN scale, in the fused
+    # quantization as in the activation quantizer: a NaN output row, the other
+    # rows unchanged, and the two-launch forward's bits
+    N = 1000
+    x = wl.activations(M, K, wl.n_outliers(K), base=3)
+    w = wl.packed_weight(4300, 3, N, K)
+    qw, sw = cr.quantize_weight(bf16_to_dev(w))
+    y0 = bits(cr.linear_fwd(bf16_to_dev(x), qw, sw))
+    xb = x.copy()
+    xb[M - 1, 5] = 0x7FC0                     # NaN
+    if M > 2:
+        xb[1, K - 1] = 0xFF80                 # -inf
+    xd = bf16_to_dev(xb)
+    y = bits(cr.linear_fwd(xd, qw, sw))
+    qx, sx = cr.quantize_act(xd)
+    assert np.array_equal(y, bits(cr.gemm_i8_bf16(qx, sx, qw, sw)))
+    bad = [M - 1] + ([1] if M > 2 else [])
+    yf = wl.bf16_bits_to_f32(y)
+    for r in bad:
+        assert np.isnan(yf[r]).all(), f"row {r} should be NaN"
+    keep = np.setdiff1d(np.arange(M), bad)
+    assert np.array_equal(y[keep], y0[keep])

@@ -166,6 +166,8 @@ namespace {
 int linear_fwd_launch(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw, const float* sw,
                       int64_t N, const uint16_t* bias, uint16_t* y, void* workspace,
                       hipStream_t stream) {
+  if (small_m_fused(M, N, K))  // one launch: q_x and s_x never leave LDS
+    return hip_status(launch_linear_fwd_small_m_fused(x, qw, sw, bias, M, N, K, y, stream));
   int8_t* qx = static_cast<int8_t*>(workspace);
   float* sx = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + align256((size_t)M * K));
   hipError_t e = launch_rotate_quant(x, M, (int)K, qx, sx, nullptr, false, false, stream);

@@ -19,6 +19,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "span_quant.h"
 
 namespace convrot {
 namespace {
@@ -110,6 +111,96 @@ __global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_kernel(
     const int64_t m = 16 * t + 4 * (l >> 4) + v;
     const int64_t nn = n0 + (l & 15);
     if (m < M && nn < N) store_out<SW>(part[t][v][l], m, nn, M, N, sx, sw, bias, y);
+  }
+}
+
+// The forward of at most eight rows in one launch, the activation's rotation
+// and quantization fused into the contraction ("Add ConvRot INT8
+// quantization", sd-scripts pull request 2461, Summary, kernels bullet: online
+// rotation and dynamic quantization inside the matmul).  Every workgroup
+// rotates and quantizes the rows of x itself, with the activation quantizer's
+// own device code (quantize_span, 16-block spans, the same split of a row over
+// waves as rotate_quant_long_kernel), so its codes and scales equal the
+// two-launch forward's bit for bit; they stay in LDS (codes row-major).  A row
+// of K values takes ceil(K / 2048) waves, so the 8 waves hold 8 / that many
+// rows.  The rows' spans arrive by direct loads issued ahead of the wave's
+// first G q_w steps, and the wait for the spans leaves those G loads in
+// flight: the quantization runs while the weight stream is on its way.  The
+// contraction and epilogue are gemm_small_m_kernel's for one row tile.
+constexpr int kFusedCodes = 16384;  // bytes of codes in LDS (rows x K)
+
+template <int G>
+__global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_fused_kernel(
+    const uint16_t* __restrict__ x, const int8_t* __restrict__ qw, const float* __restrict__ sw,
+    const uint16_t* __restrict__ bias, int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y) {
+  __shared__ __align__(16) uint8_t spans[kSmWaves][span_bytes<16>()];
+  __shared__ __align__(16) int8_t qx[kFusedCodes];
+  __shared__ float sx[kSmWaves];
+  __shared__ float row_part_max[kSmWaves];
+  __shared__ float seg_max[kSmWaves][16];
+  __shared__ int32_t part[4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int i = threadIdx.x; i < 256; i += 64 * kSmWaves) (&part[0][0])[i] = 0;
+
+  // This wave's span: blocks 16 jw .. 16 jw + 15 of row m (rows m >= M: none).
+  const int nb = (int)(K / kBlock);
+  const int wpr = (nb + 15) >> 4;
+  const int m = wave / wpr, jw = wave - m * wpr;
+  const bool has_span = m < M;
+  const int blk0 = 16 * jw;
+  const int span_blocks = nb - blk0 < 16 ? nb - blk0 : 16;
+  const int64_t span_elem0 = (int64_t)m * K + (int64_t)blk0 * kBlock;
+  if (has_span) stage_span<16, false>(x, span_elem0, span_blocks, spans[wave]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // The wave's 64-byte k-steps of its 16 q_w rows; steps past the wave's last
+  // reload the row's last step, and their products are dropped.
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n = n0 + r < N ? n0 + r : N - 1;  // columns past the end reload the last one
+  const int8_t* wrow = qw + n * K + 16 * g;
+  const int nks = (int)(K / 64);
+  const int nj = nks > wave ? (nks - wave + kSmWaves - 1) / kSmWaves : 0;
+  auto step_of = [&](int j) { return (int64_t)(j < nj ? wave + kSmWaves * j : nks - 1) * 64; };
+  uint4 wv[G];
+#pragma unroll
+  for (int u = 0; u < G; ++u) wv[u] = *reinterpret_cast<const uint4*>(wrow + step_of(u));
+  __builtin_amdgcn_sched_barrier(0);
+
+  // The span's loads are older than the G weight loads: vmcnt(G) means they landed.
+  wait_vm_n<G>();
+  if (has_span)
+    quantize_span<kRotate, 16, false>(spans[wave], span_blocks, nb, span_elem0, m, wpr, qx, sx,
+                                      seg_max[wave], row_part_max + m * wpr, nullptr, m * wpr);
+  else if (wpr > 1)
+    __syncthreads();  // a wave without a row joins the one row-maximum barrier of quantize_span
+  __syncthreads();    // every row's codes and scale are in LDS
+
+  const int8_t* xrow = qx + (int64_t)(r < M ? r : M - 1) * K + 16 * g;
+  v4i acc = v4i{0, 0, 0, 0};
+  for (int j0 = 0; j0 < nj; j0 += G) {
+    if (j0 > 0) {
+#pragma unroll
+      for (int u = 0; u < G; ++u) wv[u] = *reinterpret_cast<const uint4*>(wrow + step_of(j0 + u));
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const uint4 xv = *reinterpret_cast<const uint4*>(xrow + step_of(j0 + u));
+      const uint4 w = j0 + u < nj ? wv[u] : make_uint4(0, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, xv),
+                                                  __builtin_bit_cast(v4i, w), acc, 0, 0, 0);
+    }
+  }
+  // lane l holds rows 4 (l / 16) + v, column l % 16
+#pragma unroll
+  for (int v = 0; v < 4; ++v) atomicAdd(&part[v][lane], acc[v]);
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 256; idx += 64 * kSmWaves) {
+    const int l = idx & 63, v = idx >> 6;
+    const int64_t mm = 4 * (l >> 4) + v;
+    const int64_t nn = n0 + (l & 15);
+    if (mm < M && nn < N) store_out<false>(part[v][l], mm, nn, M, N, sx, sw, bias, y);
   }
 }
 
@@ -384,6 +475,25 @@ int small_m_mode(int64_t M, int64_t N, int64_t K) {
   // with the roles swapped, each workgroup reading 16 token rows once.
   if (N >= 1 && N <= kSmallM && M >= 2048 && M <= 0x7ffffff0) return 2;
   return 0;
+}
+
+// Rows the fused few-row forward holds: ceil(K / 2048) waves per row of the 8.
+static int fused_rows(int64_t K) { return kSmWaves / (int)((K / kBlock + 15) / 16); }
+
+bool small_m_fused(int64_t M, int64_t N, int64_t K) {
+  if (small_m_mode(M, N, K) != 1 || small_m_split(M, N, K) > 1 || K % kBlock) return false;
+  return M <= fused_rows(K) && M * K <= kFusedCodes;
+}
+
+hipError_t launch_linear_fwd_small_m_fused(const uint16_t* x, const int8_t* qw, const float* sw,
+                                           const uint16_t* bias, int64_t M, int64_t N, int64_t K,
+                                           uint16_t* y, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (!small_m_fused(M, N, K)) return hipErrorInvalidValue;
+  const int64_t grid = (N + 15) / 16;
+  hipLaunchKernelGGL(gemm_small_m_fused_kernel<8>, dim3((unsigned)grid), dim3(64 * kSmWaves), 0,
+                     stream, x, qw, sw, bias, M, N, K, y);
+  return hipGetLastError();
 }
 
 int small_m_split(int64_t M, int64_t N, int64_t K) {

@@ -73,6 +73,13 @@ int small_m_split(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_small_m(const int8_t* qx, const float* sx, const int8_t* qw,
                                const float* sw, const uint16_t* bias, int64_t M, int64_t N,
                                int64_t K, uint16_t* y, int32_t* partial, hipStream_t stream);
+// The whole forward of very few rows (at most 8 / ceil(K / 2048)) in one
+// launch: each workgroup rotates and quantizes x's rows itself, in LDS, with
+// the activation quantizer's code, then runs the few-row contraction.
+bool small_m_fused(int64_t M, int64_t N, int64_t K);
+hipError_t launch_linear_fwd_small_m_fused(const uint16_t* x, const int8_t* qw, const float* sw,
+                                           const uint16_t* bias, int64_t M, int64_t N, int64_t K,
+                                           uint16_t* y, hipStream_t stream);
 // Sum S int32 partials [S, J, I] and dequantize to out[j][i] with the forward
 // epilogue (s_j[j], then s_i[i], then bias[i]).  Needs I % 4 == 0.
 hipError_t launch_splitk_dequant(const int32_t* partial, int S, int64_t J, int64_t I,

@@ -72,13 +72,20 @@ __device__ __forceinline__ void swap_rows16(double& vdst, double& src0) {
 // register bit 4 with a lane bit, so that the butterfly partners meet in one
 // lane.  After both, lane quarter q = L >> 4 holds outputs 16 q + e in v[e]
 // and 64 + 16 q + e in v[e + 16] (e < 16).
+//
+// A row shared by several waves (waves_per_row > 1) is held by waves
+// row_wave0 .. row_wave0 + waves_per_row - 1 of the workgroup; they exchange
+// their maxima through row_part_max[0 .. waves_per_row - 1] (the row's own
+// slots) at one workgroup barrier, which every wave of the workgroup must
+// reach, and wave row_wave0 writes the row's scale.
 template <int MODE, int SB = kSpanBlocks, bool STREAM = false>
 __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_blocks, int nb,
                                               int64_t span_elem0, int64_t row0,
                                               int waves_per_row, int8_t* __restrict__ q,
                                               float* __restrict__ scale,
                                               float* seg_max_wave, float* row_part_max,
-                                              const uint8_t* cs_lds = nullptr) {
+                                              const uint8_t* cs_lds = nullptr,
+                                              int row_wave0 = 0) {
 #pragma clang fp contract(off)
   static_assert(SB == 16 || SB == 32, "a span is one or two passes of 16 blocks");
   constexpr int NP = SB / 16;  // passes
@@ -216,7 +223,7 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
     }
   } else {
     const float mw = group_max(mall, 16);
-    if (lane == 0) row_part_max[wave] = mw;
+    if (lane == 0) row_part_max[wave - row_wave0] = mw;
     __syncthreads();
     float mm = 0.f;
     for (int w = 0; w < waves_per_row; ++w) mm = max_nan(mm, row_part_max[w]);
@@ -272,7 +279,7 @@ __device__ __forceinline__ void quantize_span(const uint8_t* my_lds, int span_bl
       *reinterpret_cast<uint4*>(stg + 16 * phys(c_hi)) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
       if (waves_per_row == 1 && g == 0 && b % nb == 0) scale[row0 + b / nb] = s;
     }
-    if (k == 0 && waves_per_row > 1 && wave == 0 && lane == 0) scale[row0] = s;
+    if (k == 0 && waves_per_row > 1 && wave == row_wave0 && lane == 0) scale[row0] = s;
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): staging writes landed
   __builtin_amdgcn_wave_barrier();
