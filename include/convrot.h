@@ -111,7 +111,10 @@ int convrot_quantize_weight(const uint16_t* w, int64_t rows, int64_t cols, int32
  *              tiles, or more than 32 rows at K = 8192 on the few-row path).
  *              Which kernels run depends on M, N and K (one tiled GEMM, a
  *              few-row kernel for M <= 128 or for N <= 128, or a split along K);
- *              y is the same bit for bit on every path.
+ *              y is the same bit for bit on every path.  For at most
+ *              8 / ceil(K / 2048) rows (K <= 8192, N <= 8192) the forward is one
+ *              launch that keeps q_x and s_x on chip and leaves the workspace
+ *              untouched; its contents after a call are unspecified either way.
  */
 int convrot_linear_fwd(const uint16_t* x, int64_t M, int64_t K, const int8_t* qw,
                        const float* sw, int64_t N, const uint16_t* bias, uint16_t* y,
