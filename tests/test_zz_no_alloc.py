@@ -39,6 +39,7 @@ def _layer(cr, M, K, N, base):
     [(4096, 4096, 4096), (300, 4096, 4096)],     # tiled GEMM, then split-K
     [(20480, 4096, 4096), (77, 4096, 4096)],     # the packed stream, then the few-row kernel
     [(4096, 16384, 4096), (2048, 4096, 32)],     # MLP down input, then skinny outputs
+    [(4096, 4096, 4096), (2, 4096, 4096)],       # tiled GEMM, then the one-launch few-row forward
 ])
 def test_noalloc_matches_workspace_forward(cr, shapes):
     for i, (M, K, N) in enumerate(shapes):
