@@ -168,7 +168,10 @@ __global__ __launch_bounds__(64 * kSmWaves) void gemm_small_m_fused_kernel(
   for (int u = 0; u < G; ++u) wv[u] = *reinterpret_cast<const uint4*>(wrow + step_of(u));
   __builtin_amdgcn_sched_barrier(0);
 
-  // The span's loads are older than the G weight loads: vmcnt(G) means they landed.
+  // The span's loads are older than the G weight loads: vmcnt(G) means they
+  // landed.  This needs at least G loads issued after them: each step is one
+  // 16-byte load, and the compiler cannot merge the repeated past-the-end
+  // steps (their addresses depend on nj and K, known only at run time).
   wait_vm_n<G>();
   if (has_span)
     quantize_span<kRotate, 16, false>(spans[wave], span_blocks, nb, span_elem0, m, wpr, qx, sx,
