@@ -48,8 +48,8 @@ __global__ __launch_bounds__(64 * kDownWaves) void lora_down_kernel(
   const int nkb = (int)(K / 64);
   const int nj = nkb > wave ? (nkb - wave + kDownWaves - 1) / kDownWaves : 0;  // this wave's blocks
 
-  // Group j0 covers this wave's blocks j0 .. j0 + 3; blocks past the wave's
-  // last one reload it (valid addresses).
+  // Group j0 covers this wave's blocks j0 .. j0 + kDownGroup - 1; blocks past
+  // the wave's last one reload it (valid addresses).
   auto load = [&](int j0, DownGroup<NT>& d) {
 #pragma unroll
     for (int u = 0; u < kDownGroup; ++u) {
