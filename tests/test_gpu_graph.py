@@ -40,7 +40,7 @@ def capture(fn):
 
 
 @pytest.mark.parametrize("M,K,N", [(77, 4096, 4096), (100, 8192, 1000), (300, 4096, 4096),
-                                   (4096, 512, 2048)])
+                                   (4096, 512, 2048), (2, 4096, 4096)])
 def test_forward_graph_replays(cr, M, K, N):
     print(f"graph forward M={M} K={K} N={N}", flush=True)
     x = bf16_to_dev(wl.activations(M, K, wl.n_outliers(K), base=5))
