@@ -1,9 +1,11 @@
 """Seeded sweep of layer shapes across every dispatch boundary of the forward and
 both input gradients.
 
-The forward picks among the tiled GEMM, split-K and the few-row kernel (either
-role) from M, N and K; the shapes here are drawn around those boundaries (M near
-128 and 2048, N near 128, 2048 and 8192, K from 128 to 12288, ragged sizes).
+The forward picks among the tiled GEMM, split-K, the few-row kernel (either
+role) and, for very few rows, the one-launch forward from M, N and K; the shapes
+here are drawn around those boundaries (M near 128 and 2048, N near 128, 2048
+and 8192, K from 128 to 12288, ragged sizes, and either side of the one-launch
+row limit).
 For each shape:
   * the forward equals the one-pass stages (quantize_act, then the int8 GEMM
     with its dequantizing epilogue) bit for bit, whichever path it took;
@@ -40,6 +42,9 @@ def _shapes():
         picks.append((M, N, K))
     # few output columns over many tokens (the swapped few-row path)
     picks += [(2048, 100, 1024), (3000, 24, 2048), (4096, 128, 512)]
+    # either side of the one-launch forward's row limit, 8 / ceil(K / 2048) rows
+    picks += [(8, 640, 2048), (9, 640, 2048), (4, 1000, 4096), (5, 1000, 4096),
+              (2, 130, 6144), (3, 130, 6144), (2, 2000, 8192), (3, 2000, 8192)]
     return sorted(set(picks))
 
 
