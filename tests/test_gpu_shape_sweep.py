@@ -12,7 +12,11 @@ For each shape:
   * two sampled rows of the forward and of both input gradients match the
     oracle: exact codes, scales and int32 sums, and outputs within the 1e-2 row
     tolerance.
+CONVROT_SWEEP_EXTRA=n adds n seeded random shapes (CONVROT_SWEEP_SEED, default
+777) for a wider run by hand; the default run is the fixed list.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -45,7 +49,31 @@ def _shapes():
     # either side of the one-launch forward's row limit, 8 / ceil(K / 2048) rows
     picks += [(8, 640, 2048), (9, 640, 2048), (4, 1000, 4096), (5, 1000, 4096),
               (2, 130, 6144), (3, 130, 6144), (2, 2000, 8192), (3, 2000, 8192)]
+    picks += _extra_shapes(int(os.environ.get("CONVROT_SWEEP_EXTRA", "0")),
+                           int(os.environ.get("CONVROT_SWEEP_SEED", "777")))
     return sorted(set(picks))
+
+
+def _extra_shapes(n, seed):
+    """Opt-in wider sweep (CONVROT_SWEEP_EXTRA shapes, seed CONVROT_SWEEP_SEED):
+    a third of the shapes with at most 8 rows (the one-launch and few-row
+    forwards at many K), any N up to 9000, any multiple of 128 up to 12288 for K,
+    under the same per-case size bounds."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        r = g.random()
+        M = (int(g.integers(1, 9)) if r < 0.35 else
+             int(g.integers(9, 300)) if r < 0.6 else int(g.integers(300, 5000)))
+        N = int(g.integers(1, 9000)) if g.random() < 0.7 else int(128 * g.integers(1, 70))
+        K = int(128 * g.integers(1, 97))
+        while N * K > 1 << 25 or M * N * K > 1 << 35:
+            if K > 128 and g.random() < 0.5:
+                K = max(128, (K // 256) * 128)
+            else:
+                N = max(1, N // 2)
+        out.append((M, N, K))
+    return out
 
 
 @pytest.fixture(scope="module")
