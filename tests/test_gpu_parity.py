@@ -402,7 +402,8 @@ def test_bwd_ragged(cr, orc, M, N, K):
 # Embedding
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("V,D,T", [(1000, 4096, 300), (77, 384, 50), (10, 128, 7), (300, 8192, 40)])
+@pytest.mark.parametrize("V,D,T", [(1000, 4096, 300), (77, 384, 50), (10, 128, 7), (300, 8192, 40),
+                                   (200, 4224, 33), (500, 1152, 5003)])
 def test_embedding_lookup(cr, orc, V, D, T):
     say(f"embedding V={V} D={D} T={T}")
     E = wl.normal_bf16((V, D), wl.SIGMA_W, V, 1)
@@ -420,6 +421,30 @@ def test_embedding_lookup(cr, orc, V, D, T):
     assert int(oob.item()) == ooob == 2
     ob = bits(out)
     assert not ob[0].any() and not ob[-1].any()
+    assert_rows_close(ob, oout, "lookup")
+
+
+def test_embedding_lookup_many_ids(cr, orc):
+    # 300000 ids: each persistent lookup wave handles ~73 tokens, so every wave
+    # fetches its next 64 ids again mid-stream; out-of-range ids are spread
+    # through the stream, among repeated ones
+    V, D, T = 1000, 128, 300000
+    say(f"embedding lookup V={V} D={D} T={T}")
+    E = wl.normal_bf16((V, D), wl.SIGMA_W, 11, 1)
+    qe, se = cr.quantize_weight(bf16_to_dev(E))
+    oqe, ose, _ = orc.rotate_quantize(E)
+    ids = wl.token_ids(T, V, base=11)
+    g = np.random.default_rng(11)
+    bad = g.choice(T, 500, replace=False)
+    ids[bad] = np.where(g.random(500) < 0.5, -1 - g.integers(0, 1 << 20, 500), V + g.integers(0, 1 << 20, 500))
+    oob = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gout = Guarded((T, D), torch.bfloat16)
+    out = cr.embedding_lookup(to_dev(ids), qe, se, oob, out=gout.t)
+    gout.check("lookup")
+    oout, ooob = orc.embedding_lookup(ids, oqe, ose)
+    assert int(oob.item()) == ooob == 500
+    ob = bits(out)
+    assert not ob[bad].any()
     assert_rows_close(ob, oout, "lookup")
 
 
