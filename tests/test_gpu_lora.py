@@ -8,8 +8,10 @@ Compared with the oracle (O13):
   * y: int32 accumulators bit-exact (same GEMM as the plain forward), outputs
     within the 1e-2 row tolerance of the oracle's LoRA epilogue;
   * a zero up projection or a zero scale gives the plain forward bit for bit.
-Shapes: the tiny layer (64 x 256 x 256), a ragged one (301 x 384 x 640), both
-ranks 16 and 32, and sampled rows of the attention projection (4096^3, rank 16).
+Shapes: the tiny layer (64 x 256 x 256), ragged ones (301 x 384 x 640; one row
+at K = 128, where most down-projection waves have no k-block; 7 x 8192 x 1000,
+two load groups per wave; 259 x 4224 x 300), both ranks 16 and 32, and sampled
+rows of the attention projection (4096^3, rank 16).
 """
 import numpy as np
 import pytest
@@ -46,7 +48,8 @@ def _case(M, K, N, R, base):
     return x, w, lw["a"], lw["b"]
 
 
-@pytest.mark.parametrize("M,K,N", [(64, 256, 256), (301, 384, 640)])
+@pytest.mark.parametrize("M,K,N", [(64, 256, 256), (301, 384, 640), (1, 128, 100),
+                                   (7, 8192, 1000), (259, 4224, 300)])
 @pytest.mark.parametrize("R", [16, 32])
 def test_lora_small(cr, orc, M, K, N, R):
     x, w, a, b = _case(M, K, N, R, 0)
