@@ -97,7 +97,9 @@ int convrot_quantize_weight(const uint16_t* w, int64_t rows, int64_t cols, int32
 
 /*
  * Forward of the ConvRot linear (the fused int8 GEMM of the pull request's
- * Summary): y = bf16( fl32(acc) * s_x[m] * s_w[n] (+ bias[n]) ) with
+ * Summary): y = bf16( fl32(acc) * s_x[m] * s_w[n] (+ bias[n]) ), evaluated in fp32 as
+ * (fl32(acc) * s_w[n]) * s_x[m] (the frozen weight's scale first, so that no
+ * activation scale makes an intermediate overflow where y does not), with
  * acc[m][n] = sum_k q_x[m][k] * q_w[n][k] (int32, exact), where (q_x, s_x) is the
  * rotated per-row quantization of x computed on the fly.  Since R is orthogonal,
  * y approximates x * W^T in the unrotated basis.
@@ -148,7 +150,8 @@ int convrot_linear_fwd_noalloc(const uint16_t* x, int64_t M, int64_t K, const in
  * LoRA branch receives the unrotated input (training guide section 7.1, ConvRot
  * INT8 scope bullet):
  *   xa = bf16( x * A^T )                       (as a bf16 Linear; fp32 accumulation)
- *   y  = bf16( fl32(acc) * s_x[m] * s_w[n] (+ bias[n]) + lora_scale * (xa[m] . B[n]) )
+ *   y  = bf16( fl32(acc) * s_x[m] * s_w[n] (+ bias[n]) + lora_scale * (xa[m] . B[n]) ),
+ *        the product evaluated as in convrot_linear_fwd
  * with the base terms exactly as in convrot_linear_fwd and the LoRA term added in
  * fp32 before the single bf16 rounding.
  *   lora_a  bf16 [R, K] (down projection);  lora_b bf16 [N, R] (up projection)

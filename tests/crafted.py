@@ -70,3 +70,26 @@ def nonfinite_fold_rows(N: int, seed: int = 0):
     dy[3, 7] = wl.f32_to_bf16_bits(np.float32([2.0 ** 100]))[0]
     sw[7] = np.float32(2.0 ** 40)
     return dy, sw  # row 4 stays ordinary (its column 7 folds to a finite value)
+
+
+def crafted_rows(K: int) -> np.ndarray:
+    """Rows that pin the quantizer's corner cases, tiled over all blocks of K."""
+    def tile(entries, scale=1.0):
+        v = np.zeros(K, dtype=np.float32)
+        for b0 in range(0, K, 128):
+            for i, val in entries.items():
+                v[b0 + i] = val * scale
+        return v
+    rows = [
+        np.zeros(K, np.float32),                          # all-zero row
+        tile({0: -253.0, 1: -255.0}),                     # exact tie at 0.5
+        tile({0: 3.0, 1: 1.0}),                           # exact tie at 63.5
+        tile({0: -255.0, 1: -85.0}),                      # division vs reciprocal
+        tile({0: 1.0}),                                   # e0
+        tile({i: 1.0 for i in range(128)}),               # ones
+        tile({1: 1.0}), tile({64: -1.0}),
+        tile({0: 2.0 ** 20, 1: 2.0 ** -10, 77: -3.0}),    # wide but exact spread
+        tile({3: 1e-32, 9: -2e-32}),                      # tiny scale (IEEE division path)
+        tile({5: 1e36, 6: -3e35}),                        # huge scale (IEEE division path)
+    ]
+    return wl.f32_to_bf16_bits(np.stack(rows))

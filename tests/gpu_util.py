@@ -63,7 +63,7 @@ def assert_rows_close(gpu_bits: np.ndarray, ref_bits: np.ndarray, what: str, tol
 
 def assert_fwd_elementwise(gpu_bits: np.ndarray, ref_bits: np.ndarray, what: str):
     """Forward outputs without bias, element by element: the GPU's fp32 chain
-    fl32(fl32(fl32(acc) * s_x) * s_w) is within 3 * 2^-24 (relative) of the exact
+    fl32(fl32(fl32(acc) * s_w) * s_x) is within 3 * 2^-24 (relative) of the exact
     product, so after both sides round to bf16 they differ by at most one bf16
     ulp of the reference, i.e. |gpu - ref| <= 2^-7 * |ref|; an exact zero stays
     zero."""

@@ -32,36 +32,13 @@ def orc():
     return oracle
 
 
-from crafted import nonfinite_fold_rows, nonfinite_rows, tiny_fold_rows  # noqa: E402
+from crafted import crafted_rows, nonfinite_fold_rows, nonfinite_rows, tiny_fold_rows  # noqa: E402
 from gpu_util import (Guarded, assert_exact, assert_fwd_elementwise, assert_rows_close,  # noqa: E402
                       bf16_to_dev, bits, guarded_workspace, host, to_dev)
 
 
 def say(*a):
     print(*a, flush=True)
-
-
-def crafted_rows(K: int) -> np.ndarray:
-    """Rows that pin the quantizer's corner cases, tiled over all blocks of K."""
-    def tile(entries, scale=1.0):
-        v = np.zeros(K, dtype=np.float32)
-        for b0 in range(0, K, 128):
-            for i, val in entries.items():
-                v[b0 + i] = val * scale
-        return v
-    rows = [
-        np.zeros(K, np.float32),                          # all-zero row
-        tile({0: -253.0, 1: -255.0}),                     # exact tie at 0.5
-        tile({0: 3.0, 1: 1.0}),                           # exact tie at 63.5
-        tile({0: -255.0, 1: -85.0}),                      # division vs reciprocal
-        tile({0: 1.0}),                                   # e0
-        tile({i: 1.0 for i in range(128)}),               # ones
-        tile({1: 1.0}), tile({64: -1.0}),
-        tile({0: 2.0 ** 20, 1: 2.0 ** -10, 77: -3.0}),    # wide but exact spread
-        tile({3: 1e-32, 9: -2e-32}),                      # tiny scale (IEEE division path)
-        tile({5: 1e36, 6: -3e35}),                        # huge scale (IEEE division path)
-    ]
-    return wl.f32_to_bf16_bits(np.stack(rows))
 
 
 # --------------------------------------------------------------------------
@@ -150,6 +127,77 @@ def test_forward_nonfinite_row_gives_nan_output_row(cr):
     assert np.isnan(yf[3]).all()
     keep = np.arange(x.shape[0]) != 3
     assert np.array_equal(y[keep], y0[keep])
+
+
+def _huge_rows(M, K, base):
+    """Activation rows whose scales lie beyond 2^96 (values ~1e33 .. 3e36, where
+    fl32(acc * s_x) would leave the fp32 range although the output does not),
+    mixed with ordinary rows and the crafted corner rows."""
+    x = wl.activations(M, K, max(1, wl.n_outliers(K)), base=base)
+    f = wl.bf16_bits_to_f32(x).astype(np.float64)
+    g = np.random.default_rng(base)
+    for m in range(0, M, 2):
+        f[m] *= 10.0 ** g.uniform(33, 35.5)
+    x = wl.f32_to_bf16_bits(f.astype(np.float32))
+    return np.concatenate([x, crafted_rows(K)])
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 512, 640), (77, 4096, 1000), (2, 4096, 4096),
+                                   (4096, 256, 300), (2048, 1024, 32), (60, 8192, 256)])
+def test_forward_huge_activation_scales(cr, orc, M, K, N):
+    # split-K, the few-row kernels, the one-launch forward, the tiled GEMM and
+    # the swapped roles: every path gives the oracle's finite outputs where the
+    # plain fp32 chain would overflow, and the paths agree bit for bit
+    say(f"forward with row scales beyond 2^96 M={M} K={K} N={N}")
+    x = _huge_rows(M, K, 500 + M)
+    w = wl.packed_weight(4400 + N % 97, 4, N, K)
+    qw, sw = cr.quantize_weight(bf16_to_dev(w))
+    xd = bf16_to_dev(x)
+    y = cr.linear_fwd(xd, qw, sw)
+    qx, sx = cr.quantize_act(xd)
+    assert np.array_equal(bits(y), bits(cr.gemm_i8_bf16(qx, sx, qw, sw))), "paths differ"
+    assert float(host(sx).max()) > 2.0 ** 96
+    rows = np.unique(np.concatenate([np.arange(0, x.shape[0], max(1, x.shape[0] // 40)),
+                                     np.arange(x.shape[0] - 11, x.shape[0])]))
+    oqx, osx, _ = orc.rotate_quantize(x[rows])
+    oqw, osw, _ = orc.rotate_quantize(w)
+    assert_exact(host(qx)[rows], oqx, "q_x rows")
+    oy = orc.dequant_epilogue(orc.gemm_i8_i32(oqx, oqw), osx, osw)
+    yb = bits(y)[rows]
+    assert np.isfinite(wl.bf16_bits_to_f32(oy)).all()
+    assert np.isfinite(wl.bf16_bits_to_f32(yb)).all()
+    assert_rows_close(yb, oy, "y rows")
+    assert_fwd_elementwise(yb, oy, "y rows")
+
+
+def test_lora_forward_huge_activation_scales(cr, orc):
+    M, K, N, R = 130, 512, 384, 16
+    say("LoRA forward with row scales beyond 2^96")
+    x = _huge_rows(M, K, 77)
+    w = wl.packed_weight(4500, 5, N, K)
+    lw = wl.lora_weights(K, N, R, 5)
+    qw, sw = cr.quantize_weight(bf16_to_dev(w))
+    xd, ad, bd = bf16_to_dev(x), bf16_to_dev(lw["a"]), bf16_to_dev(lw["b"])
+    y = cr.linear_fwd_lora(xd, qw, sw, ad, bd, 0.5)
+    oqx, osx, _ = orc.rotate_quantize(x)
+    oqw, osw, _ = orc.rotate_quantize(w)
+    ref = orc.lora_epilogue(orc.gemm_i8_i32(oqx, oqw), osx, osw, bits(cr.lora_down(xd, ad)), lw["b"], 0.5)
+    assert np.isfinite(wl.bf16_bits_to_f32(bits(y))).all()
+    assert_rows_close(bits(y), ref, "y")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 384), (37, 4096, 512)])
+def test_bwd_int8_huge_gradient_scales(cr, orc, M, N, K):
+    # dY rows whose folded scales s_g lie beyond 2^96: the inverse rotation's
+    # fp32 sums stay in range and dX matches the oracle
+    say(f"int8 dX with s_g beyond 2^96 M={M} N={N} K={K}")
+    dy = wl.normal_bf16((M, N), 1e-3, M, 3)
+    f = wl.bf16_bits_to_f32(dy).astype(np.float64)
+    f[::3] *= 1e38
+    dy = wl.f32_to_bf16_bits(f.astype(np.float32))
+    w = wl.normal_bf16((N, K), wl.SIGMA_W, M, 1)
+    e = _bwd_int8(cr, orc, dy, w)
+    print(f"  max row relerr {e:.2e}", flush=True)
 
 
 def test_quantize_weight_tiny_and_chunked(cr, orc):

@@ -118,6 +118,25 @@ __device__ __forceinline__ float max_nan(float a, float b) {
 // non-finite row has one bit pattern on every path.
 constexpr uint32_t kScaleNaNBits = 0x7fc00000u;
 
+// A row scale s of the int8 input gradient's epilogue (the gradient's s_g),
+// applied to an int32 sum |acc| < 2^31 before the fp32 inverse rotation.  Up to
+// 2^96 the epilogue uses s as it is.  A larger scale is used as m * 2^e (frexp,
+// exact, m in [0.5, 1)): the products and the rotation's sums are formed with m
+// and 2^e joins the final constant 1/sqrt(128), so no intermediate leaves the
+// fp32 range where the result does not.  While values stay normal, scaling by
+// a power of two commutes with every rounding, so such rows get the plain
+// chain's result scaled exactly.  A NaN scale (a non-finite row) is used as it
+// is.  (The forward needs no split: it applies the weight's scale first.)
+constexpr float kSplitRowScale = 0x1p96f;
+struct RowScale {
+  float m;  // s, or its frexp mantissa when s > 2^96
+  int e;    // 0, or the frexp exponent
+};
+__device__ __forceinline__ RowScale row_scale(float s) {
+  const bool big = s > kSplitRowScale;
+  return {big ? __builtin_amdgcn_frexp_mantf(s) : s, big ? __builtin_amdgcn_frexp_expf(s) : 0};
+}
+
 // Cross-lane maxima of non-negative floats, NaN included (row maxima of |r|,
 // from +0 under max_nan): on such values the order of the bit patterns as
 // unsigned integers is the order of the floats, and a positive NaN's bits lie

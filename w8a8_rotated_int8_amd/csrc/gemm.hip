@@ -6,7 +6,7 @@
 // the input gradient through the int8 GEMM or through a transient bf16
 // dequantization), in four epilogue flavours:
 //   forward:         P = q_w [N, K], Q = q_x [M, K]; y[m][n] =
-//                    bf16(fl32(acc) * s_x[m] * s_w[n] (+ bias[n]))
+//                    bf16(fl32(fl32(fl32(acc) * s_w[n]) * s_x[m]) (+ bias[n]))
 //   int8 grad_x:     P = q_w read as [N, K] but contracted along its rows
 //                    (staged as is, transposed by the LDS reads), Q = q_g
 //                    [M, N]; the epilogue
@@ -133,22 +133,27 @@ __device__ __forceinline__ void tile_of(int64_t gi, int64_t gj, int64_t tile, in
 }
 
 // Dequantizing epilogue of four consecutive outputs i .. i+3 of row j:
-// v = fl32(acc) * s_j * s_i (+ bias_i), each operation rounded to fp32 in this
-// order (no contraction), so every path that uses it rounds identically.
+// v = fl32(fl32(fl32(acc) * s_i) * s_j) (+ bias_i), each operation rounded to
+// fp32 in this order (no contraction), so every path that uses it rounds
+// identically.  In the forward s_i is the weight's row scale and s_j the
+// activation's: the static weight scale comes first, so the first product stays
+// below 2^31 * s_i and no activation scale, however large, can make an
+// intermediate overflow where the result does not (only a weight scale beyond
+// ~2^96, |W| ~ 1e31, could).
 __device__ __forceinline__ void dequant4(float v[4], float sjv, const float* si,
                                          const uint16_t* bias, int64_t i, int64_t I) {
 #pragma clang fp contract(off)
   if (i + 4 <= I) {
     const float4 s4 = *reinterpret_cast<const float4*>(si + i);
-    v[0] = v[0] * sjv * s4.x;
-    v[1] = v[1] * sjv * s4.y;
-    v[2] = v[2] * sjv * s4.z;
-    v[3] = v[3] * sjv * s4.w;
+    v[0] = v[0] * s4.x * sjv;
+    v[1] = v[1] * s4.y * sjv;
+    v[2] = v[2] * s4.z * sjv;
+    v[3] = v[3] * s4.w * sjv;
   } else {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t iu = i + u < I ? i + u : I - 1;
-      v[u] = v[u] * sjv * si[iu];
+      v[u] = v[u] * si[iu] * sjv;
     }
   }
   if (bias) {
@@ -168,15 +173,15 @@ __device__ __forceinline__ void dequant4_tile(float v[4], float sjv, const float
 #pragma clang fp contract(off)
   if (i + 4 <= I) {
     const float4 s4 = *reinterpret_cast<const float4*>(si_tile + (i - i0));
-    v[0] = v[0] * sjv * s4.x;
-    v[1] = v[1] * sjv * s4.y;
-    v[2] = v[2] * sjv * s4.z;
-    v[3] = v[3] * sjv * s4.w;
+    v[0] = v[0] * s4.x * sjv;
+    v[1] = v[1] * s4.y * sjv;
+    v[2] = v[2] * s4.z * sjv;
+    v[3] = v[3] * s4.w * sjv;
   } else {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t iu = i + u < I ? i + u : I - 1;
-      v[u] = v[u] * sjv * si_tile[iu - i0];
+      v[u] = v[u] * si_tile[iu - i0] * sjv;
     }
   }
   if (bias) {
@@ -197,10 +202,10 @@ __device__ __forceinline__ void dequant4_pre(float v[4], float sjv, float4 s4,
                                              int64_t i, int64_t i0, int64_t I) {
 #pragma clang fp contract(off)
   if (i + 4 <= I) {
-    v[0] = v[0] * sjv * s4.x;
-    v[1] = v[1] * sjv * s4.y;
-    v[2] = v[2] * sjv * s4.z;
-    v[3] = v[3] * sjv * s4.w;
+    v[0] = v[0] * s4.x * sjv;
+    v[1] = v[1] * s4.y * sjv;
+    v[2] = v[2] * s4.z * sjv;
+    v[3] = v[3] * s4.w * sjv;
     if (bias) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) v[u] = v[u] + __uint_as_float((uint32_t)bias[i + u] << 16);
@@ -547,12 +552,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
       for (int y = 0; y < NJ; ++y) {
         const int jl = y * 32 + (lane & 31);
         const int64_t j = j0 + wj * TJ + jl;
-        const float sjv = sj_pre[y];
+        // a row scale beyond 2^96 enters as its mantissa, and its 2^e joins the
+        // final constant 1/sqrt(128) (exact; see row_scale)
+        const RowScale sj = row_scale(sj_pre[y]);
         float w[64];
 #pragma unroll
         for (int x = 0; x < 4; ++x)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) w[x * 16 + r] = (float)acc[x][y][r] * sjv;
+          for (int r = 0; r < 16; ++r) w[x * 16 + r] = (float)acc[x][y][r] * sj.m;
         // w index bits 0-1 -> i bits 0-1, bits 2-3 -> i bits 3-4, bits 4-5 ->
         // i bits 5-6; the lane half h is i bit 2.
 #pragma unroll
@@ -572,7 +579,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
           w[e] = u + v;
           w[e + 32] = u - v;
         }
-        const float cf = (float)kInvSqrt128;
+        const float cf = __builtin_ldexpf((float)kInvSqrt128, sj.e);
 #pragma unroll
         for (int q4 = 0; q4 < 8; ++q4) {
 #pragma unroll
@@ -610,7 +617,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
 #pragma unroll
       for (int y = 0; y < NJ; ++y) {
         const int jl = y * 32 + (lane & 31);
-        const int64_t j = j0 + wj * TJ + jl;
         float sjv = 1.f;
         if constexpr (kDequant) sjv = sj_pre[y];
 #pragma unroll

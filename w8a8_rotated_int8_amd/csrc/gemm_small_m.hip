@@ -2,7 +2,7 @@
 // the text encoder at a time, the training guide's text-encoder quantization
 // ("LoRA Training Guide for MOSS-Image", section 7.1, text encoder bullet).
 //
-// y[m][n] = bf16( fl32( fl32( float(acc[m][n]) * s_x[m] ) * s_w[n] ) (+ bias[n]) ),
+// y[m][n] = bf16( fl32( fl32( float(acc[m][n]) * s_w[n] ) * s_x[m] ) (+ bias[n]) ),
 // acc[m][n] = sum_k q_x[m][k] q_w[n][k]: the same int32 sums and the same fp32
 // epilogue operations as the tiled GEMM, so the output is identical to it.
 //
@@ -30,25 +30,26 @@ constexpr int kSmWaves = 8;
 
 // Output element (m, nn) of the contraction of the few rows (m < M) with the
 // many (nn < N).  Plain: the few rows are q_x's (tokens), the many q_w's, and
-// y[m][nn] = bf16(fl32(fl32(float(acc) * s_x[m]) * s_w[nn]) (+ bias[nn])).
+// y[m][nn] = bf16(fl32(fl32(float(acc) * s_w[nn]) * s_x[m]) (+ bias[nn])).
 // Swapped (SW, few output columns): the few rows are q_w's and the many q_x's,
 // with sx / sw / M / N passed in those roles; the same operations in the same
-// order give y[nn][m] = bf16(fl32(fl32(float(acc) * s_x[nn]) * s_w[m]) (+ bias[m])).
+// order give y[nn][m] = bf16(fl32(fl32(float(acc) * s_w[m]) * s_x[nn]) (+ bias[m])).
 template <bool SW>
 __device__ __forceinline__ void store_out(int32_t acc, int64_t m, int64_t nn, int64_t M,
                                           int64_t N, const float* __restrict__ sx,
                                           const float* __restrict__ sw,
                                           const uint16_t* __restrict__ bias,
                                           uint16_t* __restrict__ y) {
+  // the weight's scale first, then the activation's (the tiled GEMM's order)
   float f = (float)acc;
   if constexpr (SW) {
-    f = f * sw[nn];
     f = f * sx[m];
+    f = f * sw[nn];
     if (bias) f = f + __uint_as_float((uint32_t)bias[m] << 16);
     y[nn * M + m] = (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu);
   } else {
-    f = f * sx[m];
     f = f * sw[nn];
+    f = f * sx[m];
     if (bias) f = f + __uint_as_float((uint32_t)bias[nn] << 16);
     y[m * N + nn] = (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu);
   }
