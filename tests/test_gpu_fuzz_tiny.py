@@ -5,13 +5,19 @@ few columns and small tiles is drawn: the one-launch forward up to 8 rows, the
 few-row kernels, split-K and the tiled GEMM).  Activations mix random rows with
 outlier columns, all-zero rows and the crafted corner-case rows (exact ties at
 0.5 and 63.5, division against reciprocal, unit vectors, a wide exact spread,
-tiny and huge scales).  For every example:
+tiny and huge scales); some examples scale every row by its own power of ten
+between 1e-30 and 1e35 (row scales from far below 1 to far beyond 2^96, all
+outputs normal and finite).  For every example:
   * the activation codes and scales and the int32 accumulators equal the
     oracle's, the forward equals its stages bit for bit, and its output is within
     the row tolerance of the oracle (and one bf16 ulp elementwise without bias);
   * when N is a multiple of 128, both input gradients match the oracle on every
     row.
+CONVROT_FUZZ_EXAMPLES sets the number of examples (default 60) for a longer run
+by hand.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -44,8 +50,12 @@ def orc():
     return oracle
 
 
-def _activations(M, K, seed, crafted_every, zero_every):
+def _activations(M, K, seed, crafted_every, zero_every, magnitudes):
     x = wl.activations(M, K, max(1, wl.n_outliers(K)), base=seed)
+    if magnitudes:
+        f = wl.bf16_bits_to_f32(x).astype(np.float64)
+        f *= 10.0 ** np.random.default_rng(seed).uniform(-30, 35, (M, 1))
+        x = wl.f32_to_bf16_bits(f.astype(np.float32))
     special = crafted_rows(K)
     for m in range(M):
         if crafted_every and m % crafted_every == 0:
@@ -55,18 +65,20 @@ def _activations(M, K, seed, crafted_every, zero_every):
     return x
 
 
-@settings(max_examples=60, deadline=None, derandomize=True, database=None,
-          suppress_health_check=[HealthCheck.too_slow])
+@settings(max_examples=int(os.environ.get("CONVROT_FUZZ_EXAMPLES", "60")), deadline=None,
+          derandomize=True, database=None, suppress_health_check=[HealthCheck.too_slow])
 @given(M=st.integers(1, 300), N=st.integers(1, 300), kb=st.integers(1, 8),
        seed=st.integers(0, 1 << 20), crafted_every=st.sampled_from([0, 1, 3, 7]),
-       zero_every=st.sampled_from([0, 2, 5]), with_bias=st.booleans(), n128=st.booleans())
-def test_tiny_layer_property(cr, orc, M, N, kb, seed, crafted_every, zero_every, with_bias, n128):
+       zero_every=st.sampled_from([0, 2, 5]), magnitudes=st.booleans(), with_bias=st.booleans(),
+       n128=st.booleans())
+def test_tiny_layer_property(cr, orc, M, N, kb, seed, crafted_every, zero_every, magnitudes,
+                             with_bias, n128):
     K = 128 * kb
     if n128:
         N = 128 * max(1, min(2, N // 128))
     print(f"fuzz M={M} N={N} K={K} seed={seed} crafted_every={crafted_every} "
-          f"zero_every={zero_every} bias={with_bias}", flush=True)
-    x = _activations(M, K, seed, crafted_every, zero_every)
+          f"zero_every={zero_every} magnitudes={magnitudes} bias={with_bias}", flush=True)
+    x = _activations(M, K, seed, crafted_every, zero_every, magnitudes)
     w = wl.normal_bf16((N, K), wl.SIGMA_W, seed, 1)
     bias_np = wl.normal_bf16((N,), 1.0, seed, 18) if with_bias else None
     bias = bf16_to_dev(bias_np) if with_bias else None
