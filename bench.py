@@ -530,14 +530,14 @@ def time_graph_ms(torch, fn, calls=20, replays=50):
 
 def bench_small_m(cr, torch, dev, dev_normal, time_ms, wl):
     """Text-encoder shapes: one caption (M tokens) at a time, and skinny N = 32
-    outputs (few-row kernel or split-K).  At these sizes one call is two or
+    outputs (few-row kernel, 128 x 128 tiles or split-K).  At these sizes one call is two or
     three kernels of a few microseconds, faster than the host issues them, so
     the device time is taken from graph replays (``_us``); back-to-back eager
     calls (``_eager_us``) show the host-bound rate."""
     r = {}
     log("[bench] small-M / skinny-N forwards")
-    for (M, K, N) in ((1, 4096, 4096), (77, 4096, 4096), (300, 4096, 4096), (77, 4096, 12288),
-                      (77, 4096, 32), (4096, 4096, 32)):
+    for (M, K, N) in ((1, 4096, 4096), (77, 4096, 4096), (300, 4096, 4096), (1000, 4096, 4096),
+                      (77, 4096, 12288), (300, 4096, 12288), (77, 4096, 32), (4096, 4096, 32)):
         x = dev_normal((M, K), 1.0, 41)
         qw, sw = cr.quantize_weight(dev_normal((N, K), wl.SIGMA_W, 42))
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)

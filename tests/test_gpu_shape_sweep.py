@@ -1,17 +1,19 @@
 """Seeded sweep of layer shapes across every dispatch boundary of the forward and
 both input gradients.
 
-The forward picks among the tiled GEMM, split-K, the few-row kernel (either
-role) and, for very few rows, the one-launch forward from M, N and K; the shapes
-here are drawn around those boundaries (M near 128 and 2048, N near 128, 2048
-and 8192, K from 128 to 12288, ragged sizes, and either side of the one-launch
-row limit).
+The forward picks among the tiled GEMM (256 x 256 or 128 x 128 tiles), split-K,
+the few-row kernel (either role) and, for very few rows, the one-launch forward
+from M, N and K; the shapes here are drawn around those boundaries (M near 128
+and 2048, N near 128, 2048 and 8192, K from 128 to 12288, ragged sizes, either
+side of the one-launch row limit and of the tile-count limits of the small
+tiles).
 For each shape:
   * the forward equals the one-pass stages (quantize_act, then the int8 GEMM
     with its dequantizing epilogue) bit for bit, whichever path it took;
-  * two sampled rows of the forward and of both input gradients match the
-    oracle: exact codes, scales and int32 sums, and outputs within the 1e-2 row
-    tolerance.
+  * the forward's rows (all of them up to 2^28 multiply-adds, else three
+    sampled rows) and three sampled rows of both input gradients match the
+    oracle: exact codes, scales and int32 sums, outputs within the 1e-2 row
+    tolerance, and the forward within one bf16 ulp element by element.
 CONVROT_SWEEP_EXTRA=n adds n seeded random shapes (CONVROT_SWEEP_SEED, default
 777) for a wider run by hand; the default run is the fixed list.
 """
@@ -49,6 +51,12 @@ def _shapes():
     # either side of the one-launch forward's row limit, 8 / ceil(K / 2048) rows
     picks += [(8, 640, 2048), (9, 640, 2048), (4, 1000, 4096), (5, 1000, 4096),
               (2, 130, 6144), (3, 130, 6144), (2, 2000, 8192), (3, 2000, 8192)]
+    # the one-pass GEMM's tile choice: 128 x 128 tiles with four stages up to
+    # 256 tiles, with two stages up to 512, then 256 x 256; ragged edges, and
+    # N below 4 (no split-K)
+    picks += [(257, 1000, 640), (1024, 4096, 1024), (1025, 4096, 1024), (2047, 4096, 1024),
+              (2049, 4096, 1024), (1500, 4100, 512), (300, 3, 1024), (700, 1, 384),
+              (300, 4096, 4096), (1000, 4096, 4096), (1500, 4096, 4096)]
     picks += _extra_shapes(int(os.environ.get("CONVROT_SWEEP_EXTRA", "0")),
                            int(os.environ.get("CONVROT_SWEEP_SEED", "777")))
     return sorted(set(picks))
@@ -108,7 +116,10 @@ def test_shape(cr, orc, M, N, K):
     qx, sx = cr.quantize_act(xd)
     assert torch.equal(y, cr.gemm_i8_bf16(qx, sx, qw, sw)), "forward differs from its stages"
 
-    rows = np.unique(np.array([0, M - 1, (M * 5) // 7]))
+    # every forward row where the oracle's GEMM stays small, else three
+    # sampled rows (the gradients: the sampled rows)
+    sampled = np.unique(np.array([0, M - 1, (M * 5) // 7]))
+    rows = np.arange(M) if M * N * K <= 1 << 28 else sampled
     oqw, osw, _ = orc.rotate_quantize(w)
     assert_exact(host(qw), oqw, "q_w")
     assert_exact(host(sw), osw, "s_w")
@@ -128,5 +139,7 @@ def test_shape(cr, orc, M, N, K):
         dx16 = cr.linear_bwd_dx(dyd, qw, sw, cr.BWD_BF16, out=gd16.t)
         gd8.check("int8 dX")
         gd16.check("bf16 dX")
-        assert_rows_close(bits(dx8)[rows], orc.bwd_dx_int8(dy[rows], oqw, osw)["dx"], "int8 dX rows")
-        assert_rows_close(bits(dx16)[rows], orc.bwd_dx_bf16(dy[rows], oqw, osw)["dx"], "bf16 dX rows")
+        assert_rows_close(bits(dx8)[sampled], orc.bwd_dx_int8(dy[sampled], oqw, osw)["dx"],
+                          "int8 dX rows")
+        assert_rows_close(bits(dx16)[sampled], orc.bwd_dx_bf16(dy[sampled], oqw, osw)["dx"],
+                          "bf16 dX rows")

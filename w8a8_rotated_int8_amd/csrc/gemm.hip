@@ -215,36 +215,48 @@ __device__ __forceinline__ void dequant4_pre(float v[4], float sjv, float4 s4,
   }
 }
 
-// One 256 x 256 output tile; every thread of the workgroup takes part.  LDS at
-// `lds`: the operand ring (STAGES * 2 * 256 * BK bytes), plus 32 KB for the
-// LoRA epilogue or 1 KB for the tile's s_i values of the dequantizing one.
-template <int EPI, bool PT, bool BF16, int WI, int WJ, int BK, int STAGES>
+// One UI x UJ output tile (i x j; 256 x 256 unless a smaller tile gives a
+// launch more workgroups); every thread of the workgroup takes part.  LDS at
+// `lds`: the operand ring (STAGES * (UI + UJ) * BK bytes), plus 32 KB for the
+// LoRA epilogue or 4 * UI bytes for the tile's s_i values of the dequantizing
+// one.
+template <int EPI, bool PT, bool BF16, int WI, int WJ, int BK, int STAGES, int UI = kTile,
+          int UJ = kTile>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8_t* lds) {
   typedef typename AccT<BF16>::type acc_t;
   constexpr int esz = BF16 ? 2 : 1;
   constexpr int NT = 64 * WI * WJ;
-  constexpr int TI = kTile / WI, TJ = kTile / WJ;  // wave tile
-  constexpr int NI = TI / 32, NJ = TJ / 32;        // MFMA tiles per wave
-  constexpr int kStage = kTile * BK;               // bytes per operand per stage
-  constexpr int kLoadsPerStage = 2 * kTile * (BK / 16) / NT;  // DMA per thread per stage
-  static_assert(!PT || (BK == 128 && (NT == 256 || NT == 512) && STAGES == 2),
-                "transposed P: BK 128, 4 or 8 waves, 2 stages");
+  constexpr int TI = UI / WI, TJ = UJ / WJ;  // wave tile
+  constexpr int NI = TI / 32, NJ = TJ / 32;  // MFMA tiles per wave
+  constexpr int kStageP = UI * BK, kStageQ = UJ * BK;  // bytes per operand per stage
+  constexpr int kBuf = kStageP + kStageQ;              // one stage of both operands
+  constexpr int kRing = STAGES * kBuf;
+  constexpr int kLoadsPerStage = (UI + UJ) * (BK / 16) / NT;  // DMA per thread per stage
+  static_assert(UI * (BK / 16) % NT == 0 && UJ * (BK / 16) % NT == 0,
+                "every thread issues the same number of stage loads");
+  static_assert(NI >= 1 && NJ >= 1 && TI % 32 == 0 && TJ % 32 == 0, "whole 32x32 MFMA tiles");
+  static_assert(!PT || (UI == kTile && UJ == kTile && BK == 128 && (NT == 256 || NT == 512) &&
+                        STAGES == 2),
+                "transposed P: 256 x 256 tiles, BK 128, 4 or 8 waves, 2 stages");
+  static_assert(EPI != kEpiDequantLoraBf16 || (UI == kTile && UJ == kTile),
+                "LoRA epilogue: 256 x 256 tiles");
+  static_assert(EPI != kEpiDequantBf16 || UI <= NT, "one s_i per thread of the first UI");
   static_assert(EPI != kEpiInvRotBf16 || TI == 128, "inverse rotation needs 128-wide wave tiles");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wi = wave % WI, wj = wave / WI;
-  const int64_t gi = (a.I + kTile - 1) / kTile, gj = (a.J + kTile - 1) / kTile;
+  const int64_t gi = (a.I + UI - 1) / UI, gj = (a.J + UJ - 1) / UJ;
   int ti, tj;
   tile_of(gi, gj, tile, ti, tj);
-  const int64_t i0 = (int64_t)ti * kTile;
-  const int64_t j0 = (int64_t)tj * kTile;
+  const int64_t i0 = (int64_t)ti * UI;
+  const int64_t j0 = (int64_t)tj * UJ;
   const int nk = (int)(a.Kc * esz / BK);
   // Dequantizing epilogues read s_j and s_i.  Loaded there, after the main
   // loop, their latency sat in front of every store (~3 us per 4096^3
   // launch); s_j is loaded into registers now and the dequantizing kernel's
-  // 256 s_i values are copied to LDS together with the first stage.
+  // UI s_i values are copied to LDS together with the first stage.
   constexpr bool kScales =
       EPI == kEpiDequantBf16 || EPI == kEpiDequantLoraBf16 || EPI == kEpiInvRotBf16;
   // The LoRA epilogue of rank 16 leaves 16 KB of its 32 KB LDS region free,
@@ -252,7 +264,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
   constexpr bool kTileScales = EPI == kEpiDequantBf16 && !PT;
   const bool tile_scales = kTileScales || (EPI == kEpiDequantLoraBf16 && a.lora_r == 16);
   const float* const si_tile = reinterpret_cast<const float*>(
-      lds + STAGES * 2 * kTile * BK + (EPI == kEpiDequantLoraBf16 ? 2 * kTile * 32 : 0));
+      lds + kRing + (EPI == kEpiDequantLoraBf16 ? 2 * kTile * 32 : 0));
   float sj_pre[NJ];
 #pragma unroll
   for (int y = 0; y < NJ; ++y) {
@@ -262,7 +274,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
   // LoRA epilogue: the tile's 256 rows of lora_b (i) and lora_xa (j), R bf16
   // each, are copied to LDS past the operand ring now, long before the
   // epilogue reads them as MFMA fragments.
-  uint8_t* const lora_lds = lds + STAGES * 2 * kTile * BK;
+  uint8_t* const lora_lds = lds + kRing;
   if constexpr (EPI == kEpiDequantLoraBf16) {
     const int per_row = a.lora_r / 8;  // 16-byte pieces per row
     for (int c = threadIdx.x; c < 2 * kTile * per_row; c += NT) {
@@ -280,8 +292,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
 
   const uint8_t* P = static_cast<const uint8_t*>(a.P);
   const uint8_t* Q = static_cast<const uint8_t*>(a.Q);
-  auto Ps = [&](int buf) { return lds + buf * 2 * kStage; };
-  auto Qs = [&](int buf) { return lds + buf * 2 * kStage + kStage; };
+  auto Ps = [&](int buf) { return lds + buf * kBuf; };
+  auto Qs = [&](int buf) { return lds + buf * kBuf + kStageP; };
 
   acc_t acc[NI][NJ];
 #pragma unroll
@@ -295,13 +307,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
   {
     // Per-thread source pointers and LDS destinations of the stage loads,
     // computed once: a stage load is then one 64-bit add per instruction.
-    constexpr int kRowDma = kTile * (BK / 16) / NT;  // per operand per stage
-    const uint8_t* src[2 * kRowDma];
-    uint32_t dst_off[2 * kRowDma];
+    constexpr int kDmaP = UI * (BK / 16) / NT, kDmaQ = UJ * (BK / 16) / NT;  // per stage
+    const uint8_t* src[kDmaP + kDmaQ];
+    uint32_t dst_off[kDmaP + kDmaQ];
 #pragma unroll
     for (int op = 0; op < 2; ++op) {
 #pragma unroll
-      for (int it = 0; it < kRowDma; ++it) {
+      for (int it = 0; it < (op ? kDmaQ : kDmaP); ++it) {
         const int blk = it * (NT / 64) + wave;
         const int slot = blk * 64 + lane;
         if (TR && op == 0) {
@@ -322,8 +334,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
         const int64_t row0 = op ? j0 : i0, nrows = op ? a.J : a.I;
         int64_t gr = row0 + row;
         gr = gr < nrows ? gr : nrows - 1;
-        src[op * kRowDma + it] = (op ? Q : P) + gr * ((op ? a.ldq : a.ldp) * esz) + 16 * chunk;
-        dst_off[op * kRowDma + it] = (op ? kStage : 0) + blk * 1024;  // uniform
+        src[op * kDmaP + it] = (op ? Q : P) + gr * ((op ? a.ldq : a.ldp) * esz) + 16 * chunk;
+        dst_off[op * kDmaP + it] = (op ? kStageP : 0) + blk * 1024;  // uniform
       }
     }
     const uint32_t lds_base = lds_u32(lds);
@@ -331,15 +343,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
     auto issue_p = [&](int kt, int buf) {
       const int64_t kb = (int64_t)kt * BK;
       const int64_t kbp = TR ? kb * a.ldp : kb;  // P advances by rows when it is [k][i]
-      const uint32_t b0 = lds_base + buf * 2 * kStage;
+      const uint32_t b0 = lds_base + buf * kBuf;
 #pragma unroll
-      for (int d = 0; d < kRowDma; ++d) dma16(src[d] + kbp, b0 + dst_off[d]);
+      for (int d = 0; d < kDmaP; ++d) dma16(src[d] + kbp, b0 + dst_off[d]);
     };
     auto issue_q = [&](int kt, int buf) {
       const int64_t kb = (int64_t)kt * BK;
-      const uint32_t b0 = lds_base + buf * 2 * kStage;
+      const uint32_t b0 = lds_base + buf * kBuf;
 #pragma unroll
-      for (int d = kRowDma; d < 2 * kRowDma; ++d) dma16(src[d] + kb, b0 + dst_off[d]);
+      for (int d = kDmaP; d < kDmaP + kDmaQ; ++d) dma16(src[d] + kb, b0 + dst_off[d]);
     };
     auto issue = [&](int kt, int buf) {
       issue_p(kt, buf);
@@ -385,7 +397,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
     if (tile_scales) {
       // older than the stage loads, so complete once stage 0 is, and published
       // by the same barrier
-      if (wave < kTile / 64) {
+      if (wave < UI / 64) {
         const int64_t i = i0 + wave * 64 + lane;
         dma4(static_cast<const float*>(a.si) + (i < a.I ? i : a.I - 1),
              lds_u32(si_tile) + wave * 256);
@@ -461,8 +473,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
           // requests together and held the waves behind them; split, the
           // 4096^3 forward GEMM measured ~3% faster (same-box A/B, 61.8-62.5
           // vs 60.0-60.7 us).  The wait at the end of stage kt+1 still covers
-          // both halves: with two stages it waits for every outstanding load.
-          static_assert(STAGES == 2, "the split refill assumes a two-stage ring");
+          // both halves: it leaves in flight only the STAGES - 2 stages issued
+          // after stage kt+2 (with two stages it waits for every load).
+          static_assert(STAGES >= 2, "the split refill needs a second buffer");
           if (kt + STAGES < nk) issue_p(kt + STAGES, buf);
         } else {
           __builtin_amdgcn_sched_barrier(0);
@@ -509,7 +522,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
     // cache lines instead of 16 bytes of 32 different rows.
     constexpr int kRowBytes = TI * 2;
     constexpr int kChunkMask = TI / 8 - 1;
-    static_assert(WI * WJ * TJ * kRowBytes <= STAGES * 2 * kStage, "staging fits the LDS ring");
+    static_assert(WI * WJ * TJ * kRowBytes <= kRing, "staging fits the LDS ring");
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes (LoRA rows) landed
     raw_barrier();  // all waves are done with the operand ring
     uint8_t* stg = lds + wave * TJ * kRowBytes;
@@ -655,10 +668,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
   }
 }
 
-template <int EPI, bool PT, bool BF16, int WI, int WJ, int BK, int STAGES>
-__global__ __launch_bounds__(64 * WI * WJ, 1) void gemm_kernel(GemmArgs a) {
+// A smaller tile keeps its registers within two workgroups per CU.
+template <int EPI, bool PT, bool BF16, int WI, int WJ, int BK, int STAGES, int UI = kTile,
+          int UJ = kTile>
+__global__ __launch_bounds__(64 * WI * WJ, UI * UJ < kTile * kTile ? 2 : 1) void gemm_kernel(
+    GemmArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
-  gemm_tile<EPI, PT, BF16, WI, WJ, BK, STAGES>(a, blockIdx.x, lds);
+  gemm_tile<EPI, PT, BF16, WI, WJ, BK, STAGES, UI, UJ>(a, blockIdx.x, lds);
 }
 
 // Split-K: workgroup (slice s, tile t) with blockIdx = s * tiles + t contracts
@@ -704,19 +720,21 @@ __global__ __launch_bounds__(256) void splitk_dequant_kernel(const int32_t* __re
   *reinterpret_cast<uint2*>(out + j * I + i) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
-template <int EPI, bool PT, bool BF16, int WI, int WJ, int BK, int STAGES>
+template <int EPI, bool PT, bool BF16, int WI, int WJ, int BK, int STAGES, int UI = kTile,
+          int UJ = kTile>
 hipError_t launch(const GemmArgs& a, hipStream_t stream) {
   // operand ring, plus the LoRA rows of one tile (2 x 256 rows x up to 32 bf16)
-  constexpr int kLds = STAGES * 2 * kTile * BK + (EPI == kEpiDequantLoraBf16 ? 2 * kTile * 64 : 0) +
-                       (EPI == kEpiDequantBf16 && !PT ? kTile * 4 : 0);
-  auto kern = gemm_kernel<EPI, PT, BF16, WI, WJ, BK, STAGES>;
+  // or the tile's s_i values
+  constexpr int kLds = STAGES * (UI + UJ) * BK + (EPI == kEpiDequantLoraBf16 ? 2 * kTile * 64 : 0) +
+                       (EPI == kEpiDequantBf16 && !PT ? UI * 4 : 0);
+  auto kern = gemm_kernel<EPI, PT, BF16, WI, WJ, BK, STAGES, UI, UJ>;
   {
     static std::atomic<uint64_t> configured{0};
     const void* k = (const void*)kern;
     hipError_t e = set_lds_limits_once(&k, &kLds, 1, configured);
     if (e != hipSuccess) return e;
   }
-  const int64_t gi = (a.I + kTile - 1) / kTile, gj = (a.J + kTile - 1) / kTile;
+  const int64_t gi = (a.I + UI - 1) / UI, gj = (a.J + UJ - 1) / UJ;
   if (gi <= 0 || gj <= 0) return hipSuccess;
   if (gi * gj > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3((unsigned)(gi * gj)), dim3(64 * WI * WJ), kLds, stream, a);
@@ -728,6 +746,57 @@ constexpr int kBK = CONVROT_GEMM_BK, kStages = CONVROT_GEMM_STAGES;
 
 }  // namespace
 
+// Cost model of the dequantizing GEMM's launch forms inside the forward (the
+// quantizer has just written q_x, so little of it is in L2), in microseconds
+// per 4096 of K, fitted to graph-replayed forwards of out[J, I] at K = 4096
+// and 16384, J = 129 .. 4096, I = 4096 .. 16384 on one MI355X, and taken as
+// linear in K:
+//  * 256 x 256 tiles (8 waves, one workgroup per CU): ~44 us up to 128 tiles,
+//    ~51 us towards 192;
+//  * 128 x 128 tiles with a four-stage ring (4 waves, 128 KB of LDS, one
+//    workgroup per CU) up to 256 tiles: ~17 us up to 64 tiles plus ~0.0375 us
+//    per further tile.  Two stages left the loads exposed when q_x and the
+//    weights come from beyond L2 (M = 300: 24.6 against 18.8 us);
+//  * 128 x 128 tiles with two stages (64 KB, two workgroups per CU) beyond 256
+//    tiles: ~28 us at 256 and ~0.0445 us per further tile up to 512; beyond
+//    that a third round of workgroups made it slower than 256 x 256 tiles
+//    (M = 2500: ~58 against ~47 us), so it is not used there;
+//  * split-K over 256 x 256 tiles: ~13.8 us per workgroup besides its K-slice
+//    (prologue and int32 partial stores), 8.1 ns per contraction byte with up
+//    to 128 workgroups and 12.5 ns with the whole chip busy, plus the reduce
+//    launch reading the partials at ~3.8 TB/s.
+// A 256 x 256 tile does ~1.5x less LDS traffic per multiply-add, so it wins
+// once the launch fills the chip (from ~192 tiles); before that, smaller tiles
+// put more CUs to work.
+namespace {
+
+double est_tiles256(int64_t t, int64_t K) { return (double)K / 4096.0 * (t <= 128 ? 44.0 : 51.0); }
+double est_tiles128(int64_t t, int64_t K) {
+  if (t > 512) return 1e30;
+  const double g = t <= 256 ? 17.0 + (double)(t > 64 ? t - 64 : 0) * 0.0375
+                            : 28.0 + (double)(t - 256) * 0.0445;
+  return (double)K / 4096.0 * g;
+}
+double est_splitk(int64_t t256, int S, int64_t M, int64_t N, int64_t K) {
+  const int64_t W = t256 * S;
+  const double per_byte = W <= 128   ? 0.0081
+                          : W >= 256 ? 0.0125
+                                     : 0.0081 + (double)(W - 128) * (0.0125 - 0.0081) / 128.0;
+  const double waves = (double)((W + 255) / 256);
+  return waves * (13.8 + (double)(K / S) * per_byte) + (double)S * M * N * 4.0 / 3.8e6;
+}
+int64_t tiles_of(int64_t I, int64_t J, int64_t u) { return ((I + u - 1) / u) * ((J + u - 1) / u); }
+
+}  // namespace
+
+int dequant_tile(int64_t I, int64_t J, int64_t K) {
+  const int64_t t256 = tiles_of(I, J, 256);
+  if (t256 >= 192) return kTile256x256;
+  const int64_t t128 = tiles_of(I, J, 128);
+  if (est_tiles128(t128, K) >= est_tiles256(t256, K)) return kTile256x256;
+  return t128 <= 256 ? kTile128x128Deep : kTile128x128;
+}
+
 hipError_t launch_gemm_i8(const GemmArgs& a, int epilogue, bool p_transposed, hipStream_t stream) {
   if (p_transposed) {
     if (epilogue == kEpiI32) return launch<kEpiI32, true, false, 2, 4, 128, 2>(a, stream);
@@ -735,8 +804,13 @@ hipError_t launch_gemm_i8(const GemmArgs& a, int epilogue, bool p_transposed, hi
     return hipErrorInvalidValue;
   }
   if (epilogue == kEpiI32) return launch<kEpiI32, false, false, kWI, kWJ, kBK, kStages>(a, stream);
-  if (epilogue == kEpiDequantBf16)
-    return launch<kEpiDequantBf16, false, false, kWI, kWJ, kBK, kStages>(a, stream);
+  if (epilogue == kEpiDequantBf16) {
+    switch (dequant_tile(a.I, a.J, a.Kc)) {
+      case kTile128x128Deep: return launch<kEpiDequantBf16, false, false, 2, 2, 128, 4, 128, 128>(a, stream);
+      case kTile128x128: return launch<kEpiDequantBf16, false, false, 2, 2, 128, 2, 128, 128>(a, stream);
+      default: return launch<kEpiDequantBf16, false, false, kWI, kWJ, kBK, kStages>(a, stream);
+    }
+  }
   if (epilogue == kEpiDequantLoraBf16) {
     if (a.lora_r != 16 && a.lora_r != 32) return hipErrorInvalidValue;
     return launch<kEpiDequantLoraBf16, false, false, kWI, kWJ, kBK, kStages>(a, stream);
@@ -781,20 +855,18 @@ hipError_t launch_splitk_dequant(const int32_t* partial, int S, int64_t J, int64
 }
 
 int splitk_factor(int64_t M, int64_t N, int64_t K) {
-  // Pick S (a divisor of K/128, at most 32) minimising a simple cost model of
-  // the split launch: waves of 256 workgroups over a K-slice each (~10.7 ns per
-  // contraction byte of one tile, measured), plus writing and reading the
-  // int32 partials at ~5 TB/s.  S = 1 keeps the one-pass GEMM.
-  const int64_t tiles = ((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile);
-  if (tiles >= 128 || N % 4 || small_m_mode(M, N, K)) return 1;
+  // S (a divisor of K/128, at most 32) where the cost model above puts the
+  // split launch below the best one-pass tile; S = 1 keeps the one pass.
+  const int64_t t256 = tiles_of(N, M, 256);
+  if (t256 >= 128 || N % 4 || small_m_mode(M, N, K)) return 1;
   const int64_t kb = K / kBlock;
   int best = 1;
-  double best_t = 0.0;
-  for (int S = 1; S <= 32 && S <= kb; ++S) {
+  double best_t = dequant_tile(N, M, K) == kTile256x256 ? est_tiles256(t256, K)
+                                                         : est_tiles128(tiles_of(N, M, 128), K);
+  for (int S = 2; S <= 32 && S <= kb; ++S) {
     if (kb % S) continue;
-    const double waves = (double)((tiles * S + 255) / 256);
-    const double t = waves * (double)(K / S) * 0.0107 + (S > 1 ? (double)S * M * N * 8.0 / 5.0e6 : 0.0);
-    if (S == 1 || t < best_t) {
+    const double t = est_splitk(t256, S, M, N, K);
+    if (t < best_t) {
       best = S;
       best_t = t;
     }
