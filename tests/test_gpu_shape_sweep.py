@@ -1,7 +1,7 @@
 """Seeded sweep of layer shapes across every dispatch boundary of the forward and
 both input gradients.
 
-The forward picks among the tiled GEMM (256 x 256 or 128 x 128 tiles), split-K,
+The forward picks among the tiled GEMM (256 x 256, 128 x 128 or 128 x 64 tiles), split-K,
 the few-row kernel (either role) and, for very few rows, the one-launch forward
 from M, N and K; the shapes here are drawn around those boundaries (M near 128
 and 2048, N near 128, 2048 and 8192, K from 128 to 12288, ragged sizes, either
@@ -51,11 +51,12 @@ def _shapes():
     # either side of the one-launch forward's row limit, 8 / ceil(K / 2048) rows
     picks += [(8, 640, 2048), (9, 640, 2048), (4, 1000, 4096), (5, 1000, 4096),
               (2, 130, 6144), (3, 130, 6144), (2, 2000, 8192), (3, 2000, 8192)]
-    # the one-pass GEMM's tile choice: 128 x 128 tiles with four stages up to
-    # 256 tiles, with two stages up to 512, then 256 x 256; ragged edges, and
-    # N below 4 (no split-K)
+    # the one-pass GEMM's tile choice: 128 x 64 tiles up to 256 tiles, 128 x 128
+    # tiles with four stages up to 256 tiles, with two stages up to 512, then
+    # 256 x 256; ragged edges, and N below 4 (no split-K)
     picks += [(257, 1000, 640), (1024, 4096, 1024), (1025, 4096, 1024), (2047, 4096, 1024),
               (2049, 4096, 1024), (1500, 4100, 512), (300, 3, 1024), (700, 1, 384),
+              (512, 4096, 1024), (513, 4096, 1024), (65, 8200, 256), (300, 32, 2048),
               (300, 4096, 4096), (1000, 4096, 4096), (1500, 4096, 4096)]
     picks += _extra_shapes(int(os.environ.get("CONVROT_SWEEP_EXTRA", "0")),
                            int(os.environ.get("CONVROT_SWEEP_SEED", "777")))

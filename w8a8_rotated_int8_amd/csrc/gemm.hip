@@ -753,6 +753,9 @@ constexpr int kBK = CONVROT_GEMM_BK, kStages = CONVROT_GEMM_STAGES;
 // linear in K:
 //  * 256 x 256 tiles (8 waves, one workgroup per CU): ~44 us up to 128 tiles,
 //    ~51 us towards 192;
+//  * 128 x 64 tiles (i x j) with a four-stage ring (4 waves of 64 x 32, 96 KB
+//    of LDS, one workgroup per CU) up to 256 tiles: ~12.9 us up to 96 tiles
+//    plus ~0.0194 us per further tile (five stages measured slower);
 //  * 128 x 128 tiles with a four-stage ring (4 waves, 128 KB of LDS, one
 //    workgroup per CU) up to 256 tiles: ~17 us up to 64 tiles plus ~0.0375 us
 //    per further tile.  Two stages left the loads exposed when q_x and the
@@ -765,9 +768,10 @@ constexpr int kBK = CONVROT_GEMM_BK, kStages = CONVROT_GEMM_STAGES;
 //    (prologue and int32 partial stores), 8.1 ns per contraction byte with up
 //    to 128 workgroups and 12.5 ns with the whole chip busy, plus the reduce
 //    launch reading the partials at ~3.8 TB/s.
-// A 256 x 256 tile does ~1.5x less LDS traffic per multiply-add, so it wins
-// once the launch fills the chip (from ~192 tiles); before that, smaller tiles
-// put more CUs to work.
+// A 256 x 256 tile does ~1.5x less LDS traffic per multiply-add than a
+// 128 x 128 one (and that one ~1.3x less than 128 x 64), so the larger tile
+// wins once its launch fills the chip; before that, smaller tiles put more CUs
+// to work.
 namespace {
 
 double est_tiles256(int64_t t, int64_t K) { return (double)K / 4096.0 * (t <= 128 ? 44.0 : 51.0); }
@@ -777,6 +781,10 @@ double est_tiles128(int64_t t, int64_t K) {
                             : 28.0 + (double)(t - 256) * 0.0445;
   return (double)K / 4096.0 * g;
 }
+double est_tiles64(int64_t t, int64_t K) {
+  if (t > 256) return 1e30;
+  return (double)K / 4096.0 * (12.9 + (double)(t > 96 ? t - 96 : 0) * 0.0194);
+}
 double est_splitk(int64_t t256, int S, int64_t M, int64_t N, int64_t K) {
   const int64_t W = t256 * S;
   const double per_byte = W <= 128   ? 0.0081
@@ -785,17 +793,32 @@ double est_splitk(int64_t t256, int S, int64_t M, int64_t N, int64_t K) {
   const double waves = (double)((W + 255) / 256);
   return waves * (13.8 + (double)(K / S) * per_byte) + (double)S * M * N * 4.0 / 3.8e6;
 }
-int64_t tiles_of(int64_t I, int64_t J, int64_t u) { return ((I + u - 1) / u) * ((J + u - 1) / u); }
+int64_t tiles_of(int64_t I, int64_t J, int64_t ui, int64_t uj) {
+  return ((I + ui - 1) / ui) * ((J + uj - 1) / uj);
+}
+// The one-pass form the model puts first, and its estimate.
+int one_pass_tile(int64_t I, int64_t J, int64_t K, double* est) {
+  const int64_t t256 = tiles_of(I, J, 256, 256), t128 = tiles_of(I, J, 128, 128);
+  int best = kTile256x256;
+  double e = est_tiles256(t256, K);
+  if (t256 < 192) {
+    const double e128 = est_tiles128(t128, K), e64 = est_tiles64(tiles_of(I, J, 128, 64), K);
+    if (e128 < e) {
+      best = t128 <= 256 ? kTile128x128Deep : kTile128x128;
+      e = e128;
+    }
+    if (e64 < e) {
+      best = kTile128x64;
+      e = e64;
+    }
+  }
+  if (est) *est = e;
+  return best;
+}
 
 }  // namespace
 
-int dequant_tile(int64_t I, int64_t J, int64_t K) {
-  const int64_t t256 = tiles_of(I, J, 256);
-  if (t256 >= 192) return kTile256x256;
-  const int64_t t128 = tiles_of(I, J, 128);
-  if (est_tiles128(t128, K) >= est_tiles256(t256, K)) return kTile256x256;
-  return t128 <= 256 ? kTile128x128Deep : kTile128x128;
-}
+int dequant_tile(int64_t I, int64_t J, int64_t K) { return one_pass_tile(I, J, K, nullptr); }
 
 hipError_t launch_gemm_i8(const GemmArgs& a, int epilogue, bool p_transposed, hipStream_t stream) {
   if (p_transposed) {
@@ -806,6 +829,7 @@ hipError_t launch_gemm_i8(const GemmArgs& a, int epilogue, bool p_transposed, hi
   if (epilogue == kEpiI32) return launch<kEpiI32, false, false, kWI, kWJ, kBK, kStages>(a, stream);
   if (epilogue == kEpiDequantBf16) {
     switch (dequant_tile(a.I, a.J, a.Kc)) {
+      case kTile128x64: return launch<kEpiDequantBf16, false, false, 2, 2, 128, 4, 128, 64>(a, stream);
       case kTile128x128Deep: return launch<kEpiDequantBf16, false, false, 2, 2, 128, 4, 128, 128>(a, stream);
       case kTile128x128: return launch<kEpiDequantBf16, false, false, 2, 2, 128, 2, 128, 128>(a, stream);
       default: return launch<kEpiDequantBf16, false, false, kWI, kWJ, kBK, kStages>(a, stream);
@@ -857,12 +881,12 @@ hipError_t launch_splitk_dequant(const int32_t* partial, int S, int64_t J, int64
 int splitk_factor(int64_t M, int64_t N, int64_t K) {
   // S (a divisor of K/128, at most 32) where the cost model above puts the
   // split launch below the best one-pass tile; S = 1 keeps the one pass.
-  const int64_t t256 = tiles_of(N, M, 256);
+  const int64_t t256 = tiles_of(N, M, 256, 256);
   if (t256 >= 128 || N % 4 || small_m_mode(M, N, K)) return 1;
   const int64_t kb = K / kBlock;
   int best = 1;
-  double best_t = dequant_tile(N, M, K) == kTile256x256 ? est_tiles256(t256, K)
-                                                         : est_tiles128(tiles_of(N, M, 128), K);
+  double best_t = 0.0;
+  one_pass_tile(N, M, K, &best_t);
   for (int S = 2; S <= 32 && S <= kb; ++S) {
     if (kb % S) continue;
     const double t = est_splitk(t256, S, M, N, K);

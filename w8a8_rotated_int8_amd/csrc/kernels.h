@@ -54,11 +54,11 @@ struct GemmArgs {
 // int8 operands (MFMA i32 32x32x32).  p_transposed: P is given as [Kc, I].
 hipError_t launch_gemm_i8(const GemmArgs& a, int epilogue, bool p_transposed, hipStream_t stream);
 // Output tile (i x j) of the one-pass dequantizing int8 GEMM out[J, I] over
-// K: 256 x 256 once the launch fills the chip, else 128 x 128 where the cost
-// model puts it ahead, with a four-stage operand ring up to 256 tiles (one
-// workgroup per CU) and two stages beyond (two per CU).  The tile changes no
-// result.
-enum GemmTile { kTile256x256 = 0, kTile128x128 = 1, kTile128x128Deep = 2 };
+// K: 256 x 256 once the launch fills the chip, else 128 x 128 or 128 x 64
+// where the cost model puts them ahead, with a four-stage operand ring up to
+// 256 tiles (one workgroup per CU); 128 x 128 keeps two stages beyond that
+// (two per CU).  The tile changes no result.
+enum GemmTile { kTile256x256 = 0, kTile128x128 = 1, kTile128x128Deep = 2, kTile128x64 = 3 };
 int dequant_tile(int64_t I, int64_t J, int64_t K);
 // Split-K int8 GEMM with the dequantizing epilogue (kEpiDequantBf16
 // semantics, bit-identical results): S K-slices into int32 partials
