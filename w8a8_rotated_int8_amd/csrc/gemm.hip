@@ -15,10 +15,12 @@
 //   raw int32:       test and timing hook
 //   bf16 grad_x:     bf16 operands, fp32 accumulation
 //
-// Tiling: a 256 x 256 output tile per workgroup.  WI x WJ waves split it into
-// wave tiles of (256/WI) x (256/WJ), each a grid of 32x32 MFMA tiles.  The
-// contraction advances BK bytes per stage through a ring of STAGES LDS
-// buffers; loads run STAGES-1 stages ahead of the MFMAs.  Row-major operands
+// Tiling: a UI x UJ output tile per workgroup (256 x 256; the dequantizing
+// forward also has 128 x 128 and 128 x 64 forms for launches that would leave
+// CUs idle).  WI x WJ waves split it into wave tiles of (UI/WI) x (UJ/WJ),
+// each a grid of 32x32 MFMA tiles.  The contraction advances BK bytes per
+// stage through a ring of STAGES LDS buffers; loads run STAGES-1 stages ahead
+// of the MFMAs.  Row-major operands
 // are staged with direct 16-byte global->LDS loads.  LDS rows (BK bytes) are
 // XOR-swizzled at 16-byte granularity so that the MFMA fragment reads (32
 // consecutive rows, one 16-byte chunk each) hit distinct banks.  P is the MFMA
