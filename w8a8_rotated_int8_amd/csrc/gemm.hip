@@ -242,7 +242,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t tile, uint8
                 "transposed P: 256 x 256 tiles, BK 128, 4 or 8 waves, 2 stages");
   static_assert(EPI != kEpiDequantLoraBf16 || (UI == kTile && UJ == kTile),
                 "LoRA epilogue: 256 x 256 tiles");
-  static_assert(EPI != kEpiDequantBf16 || UI <= NT, "one s_i per thread of the first UI");
+  static_assert(EPI != kEpiDequantBf16 || UI <= NT, "UI / 64 waves load the tile's s_i values");
   static_assert(EPI != kEpiInvRotBf16 || TI == 128, "inverse rotation needs 128-wide wave tiles");
 
   const int tid = threadIdx.x;
@@ -770,10 +770,10 @@ constexpr int kBK = CONVROT_GEMM_BK, kStages = CONVROT_GEMM_STAGES;
 //    (prologue and int32 partial stores), 8.1 ns per contraction byte with up
 //    to 128 workgroups and 12.5 ns with the whole chip busy, plus the reduce
 //    launch reading the partials at ~3.8 TB/s.
-// A 256 x 256 tile does ~1.5x less LDS traffic per multiply-add than a
-// 128 x 128 one (and that one ~1.3x less than 128 x 64), so the larger tile
-// wins once its launch fills the chip; before that, smaller tiles put more CUs
-// to work.
+// A 256 x 256 tile moves ~1.5x fewer LDS bytes per multiply-add than a
+// 128 x 128 one, and that one ~1.5x fewer than 128 x 64 (direct loads plus
+// fragment reads), so the larger tile wins once its launch fills the chip;
+// before that, smaller tiles put more CUs to work.
 namespace {
 
 double est_tiles256(int64_t t, int64_t K) { return (double)K / 4096.0 * (t <= 128 ? 44.0 : 51.0); }
