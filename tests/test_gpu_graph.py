@@ -4,7 +4,8 @@ Every entry point is stream-ordered and allocates nothing, so a caller may
 capture it (bench.py times the few-row forwards that way).  Each graph is
 replayed several times with eager work on the same buffers in between, and every
 replay must reproduce the eager result bit for bit: one case per forward path
-(few-row kernel, its split form, split-K, tiled GEMM) and the int8 backward.
+(few-row kernel, its split form, each GEMM tile form, split-K, the one-launch
+forward) and the int8 backward.
 """
 import pytest
 
@@ -39,8 +40,11 @@ def capture(fn):
     return g
 
 
+# few-row kernel, its split form, 128 x 64 tiles, 128 x 128 tiles with two and
+# with four stages, split-K, 256 x 256 tiles, the one-launch forward
 @pytest.mark.parametrize("M,K,N", [(77, 4096, 4096), (100, 8192, 1000), (300, 4096, 4096),
-                                   (4096, 512, 2048), (2, 4096, 4096)])
+                                   (4096, 512, 2048), (1000, 1024, 4096), (300, 16384, 4096),
+                                   (3072, 1024, 4096), (2, 4096, 4096)])
 def test_forward_graph_replays(cr, M, K, N):
     print(f"graph forward M={M} K={K} N={N}", flush=True)
     x = bf16_to_dev(wl.activations(M, K, wl.n_outliers(K), base=5))

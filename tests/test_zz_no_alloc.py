@@ -36,7 +36,8 @@ def _layer(cr, M, K, N, base):
 
 
 @pytest.mark.parametrize("shapes", [
-    [(4096, 4096, 4096), (300, 4096, 4096)],     # tiled GEMM, then split-K
+    [(4096, 4096, 4096), (300, 16384, 4096)],    # 256 x 256 tiles, then split-K
+    [(1000, 4096, 4096), (300, 4096, 4096)],     # 128 x 128 tiles, then 128 x 64 tiles
     [(20480, 4096, 4096), (77, 4096, 4096)],     # the packed stream, then the few-row kernel
     [(4096, 16384, 4096), (2048, 4096, 32)],     # MLP down input, then skinny outputs
     [(4096, 4096, 4096), (2, 4096, 4096)],       # tiled GEMM, then the one-launch few-row forward
