@@ -273,3 +273,35 @@ def test_noalloc_forward_host_checks(cr):
     m = re.search(r"#define CONVROT_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
                   open(HEADER).read())
     assert m and int(m.group(1)) << int(m.group(2)) == limit
+
+
+def test_modules_refuse_before_the_c_abi(cr, monkeypatch):
+    """The PyTorch modules check dtypes and shapes before any call reaches the
+    library: a non-bf16 activation (the bug sd-scripts pull request 2461 fixed)
+    and non-integer ids raise with nothing enqueued."""
+    import torch
+    from w8a8_rotated_int8_amd.nn import ConvRotEmbedding, ConvRotLinear
+
+    class Spy:
+        def __getattr__(self, name):
+            raise AssertionError(f"reached the C ABI: {name}")
+
+    monkeypatch.setattr(cr, "_lib", Spy())
+    qw = torch.zeros((256, 384), dtype=torch.int8)
+    sw = torch.ones(256, dtype=torch.float32)
+    mod = ConvRotLinear(qw, sw, bwd_mode="int8")
+    assert (mod.in_features, mod.out_features) == (384, 256)
+    for dt in (torch.float16, torch.float32, torch.int8):
+        with pytest.raises(TypeError):
+            mod(torch.zeros((4, 384), dtype=dt))
+    with pytest.raises(ValueError):
+        mod(torch.zeros((4, 256), dtype=torch.bfloat16))  # wrong feature count
+    with pytest.raises(ValueError):
+        ConvRotLinear(qw, sw, bwd_mode="fp8")
+    with pytest.raises(ValueError):
+        ConvRotLinear(torch.zeros((256, 200), dtype=torch.int8), sw)  # K not a multiple of 128
+    with pytest.raises(ValueError):
+        ConvRotLinear(qw, sw, bias=torch.zeros(256, dtype=torch.float32))
+    emb = ConvRotEmbedding(torch.zeros((10, 128), dtype=torch.int8), torch.ones(10))
+    with pytest.raises(TypeError):
+        emb(torch.zeros(3, dtype=torch.float32))
