@@ -1,7 +1,12 @@
 """GPU parity at the full workload sizes, through the same C-ABI calls bench.py
-times.  Quantizers are compared in full (bit-exact codes and scales); GEMM
-outputs on seeded sampled rows that the oracle computes one by one (bit-exact
-int32 accumulators, outputs within the 1e-2 row tolerance).
+times.  Quantizers are compared in full (bit-exact codes and scales).  The int8
+GEMMs of the MLP pair and of the first packed layer are compared on every row
+(bit-exact int32 accumulators, outputs within the 1e-2 row tolerance and the
+forward's one-ulp elementwise bound); the other packed layers and the bf16
+input gradients on seeded sampled rows that the oracle computes one by one.
+The oracle's accumulators of the input gradient, sum_n q_g[m][n] q_w[n][k],
+come from its row-major triple loop applied to q_w transposed (the same sums,
+in the same order over n).
 
 Workloads: the MLP pair (up [16384,4096], down [4096,16384], 4096 tokens; the
 down input is the bf16 GELU of the unquantized up projection), the packed
@@ -99,13 +104,13 @@ def test_mlp_forward(cr, orc, mlp, which):
         say(f"  rows with inexact binary64 rotation sums: {bad} of {xin.shape[0]}")
     assert_exact(host(sx), osx, "s_x")
     assert_exact(host(qx), oqx, "q_x")
-    rows = sample_rows(4096, 30, 11 if which == "up" else 12)
     acc = cr.gemm_i8_i32(qx, qw, 0)
-    oacc = orc.gemm_i8_i32(oqx, oq, rows)
-    assert_exact(host(acc)[rows], oacc, "acc (sampled rows)")
-    oy = orc.dequant_epilogue(oacc, osx, os_, rows)
-    e = assert_rows_close(bits(y)[rows], oy, "y")
-    assert_fwd_elementwise(bits(y)[rows], oy, "y")
+    say("  oracle int32 GEMM, every row")
+    oacc = orc.gemm_i8_i32(oqx, oq)
+    assert_exact(host(acc), oacc, "acc (all rows)")
+    oy = orc.dequant_epilogue(oacc, osx, os_)
+    e = assert_rows_close(bits(y), oy, "y (all rows)")
+    assert_fwd_elementwise(bits(y), oy, "y (all rows)")
     say(f"  max row relerr {e:.2e}")
 
 
@@ -123,11 +128,11 @@ def test_mlp_int8_grad(cr, orc, mlp, which):
     oqg, osg = orc.bwd_quant_dy(dy, os_)
     assert_exact(host(sg), osg, "s_g")
     assert_exact(host(qg), oqg, "q_g")
-    rows = sample_rows(4096, 14, 21 if which == "down" else 22)
     acc2 = cr.gemm_i8_i32(qg, qw, 1)
-    oacc2 = orc.gemm_i8_i32_rows_of_b(oqg, oq, rows)
-    assert_exact(host(acc2)[rows], oacc2, "acc2 (sampled rows)")
-    e = assert_rows_close(bits(dx)[rows], orc.bwd_int8_epilogue(oacc2, osg, rows), "dX int8")
+    say("  oracle int32 GEMM along q_w's rows, every row")
+    oacc2 = orc.gemm_i8_i32(oqg, np.ascontiguousarray(oq.T))
+    assert_exact(host(acc2), oacc2, "acc2 (all rows)")
+    e = assert_rows_close(bits(dx), orc.bwd_int8_epilogue(oacc2, osg), "dX int8 (all rows)")
     say(f"  max row relerr {e:.2e}")
 
 
@@ -180,11 +185,12 @@ def test_packed_layer(cr, orc, packed, layer):
     xd = bf16_to_dev(p["x"])
     y = cr.linear_fwd(xd, qw, sw)
     qx, _ = cr.quantize_act(xd)
-    rows = sample_rows(20480, 22, 40 + layer)
+    # the first layer on every row, the others on seeded sampled rows
+    rows = np.arange(20480) if layer == 0 else sample_rows(20480, 22, 40 + layer)
     acc = cr.gemm_i8_i32(qx, qw, 0)
-    oacc = orc.gemm_i8_i32(packed["oqx"], oq, rows)
+    oacc = orc.gemm_i8_i32(packed["oqx"], oq, None if layer == 0 else rows)
     assert_exact(host(acc)[rows], oacc, "acc")
-    oy = orc.dequant_epilogue(oacc, packed["osx"], os_, rows)
+    oy = orc.dequant_epilogue(oacc, packed["osx"], os_, None if layer == 0 else rows)
     assert_rows_close(bits(y)[rows], oy, "y")
     assert_fwd_elementwise(bits(y)[rows], oy, "y")
     dyd = bf16_to_dev(p["dy"])
@@ -194,9 +200,14 @@ def test_packed_layer(cr, orc, packed, layer):
     assert_exact(host(sg), osg, "s_g")
     assert_exact(host(qg), oqg, "q_g")
     acc2 = cr.gemm_i8_i32(qg, qw, 1)
-    oacc2 = orc.gemm_i8_i32_rows_of_b(oqg, oq, rows)
-    assert_exact(host(acc2)[rows], oacc2, "acc2")
-    assert_rows_close(bits(dx)[rows], orc.bwd_int8_epilogue(oacc2, osg, rows), "dX int8")
+    if layer == 0:
+        oacc2 = orc.gemm_i8_i32(oqg, np.ascontiguousarray(oq.T))
+        assert_exact(host(acc2), oacc2, "acc2 (all rows)")
+        assert_rows_close(bits(dx), orc.bwd_int8_epilogue(oacc2, osg), "dX int8 (all rows)")
+    else:
+        oacc2 = orc.gemm_i8_i32_rows_of_b(oqg, oq, rows)
+        assert_exact(host(acc2)[rows], oacc2, "acc2")
+        assert_rows_close(bits(dx)[rows], orc.bwd_int8_epilogue(oacc2, osg, rows), "dX int8")
     # the default backward: transient bf16 W_hat, bf16 GEMM over the 20480 tokens
     dx16 = cr.linear_bwd_dx(dyd, qw, sw, cr.BWD_BF16)
     owhat = orc.dequant_weight(oq, os_)

@@ -301,8 +301,9 @@ def test_linear_fwd_ragged(cr, orc, M, N, K):
 
 
 def test_linear_fwd_attn_full_size(cr, orc):
-    """The attention-projection workload at full size: all codes and scales
-    exact, int32 accumulators and outputs on 64 seeded rows (incl. both ends)."""
+    """The attention-projection workload at full size, the configuration the
+    headline measures: all codes, scales and int32 accumulators exact, every
+    output within the row tolerance and one bf16 ulp elementwise."""
     a = wl.attn(0)
     say("linear_fwd attn 4096^3")
     xd, wd = bf16_to_dev(a["x"]), bf16_to_dev(a["w"])
@@ -320,13 +321,12 @@ def test_linear_fwd_attn_full_size(cr, orc):
     assert bad == 0
     assert_exact(host(qx), oqx, "q_x")
     assert_exact(host(sx), osx, "s_x")
-    rows = np.unique(np.concatenate([[0, 1, 4095], np.random.default_rng(0).choice(4096, 61, False)]))
     acc = cr.gemm_i8_i32(qx, qw, 0)
-    oacc = orc.gemm_i8_i32(oqx, oqw, rows)
-    assert_exact(host(acc)[rows], oacc, "acc (sampled rows)")
-    oy = orc.dequant_epilogue(oacc, osx, osw, rows)
-    e = assert_rows_close(bits(y)[rows], oy, "y (sampled rows)")
-    assert_fwd_elementwise(bits(y)[rows], oy, "y (sampled rows)")
+    oacc = orc.gemm_i8_i32(oqx, oqw)
+    assert_exact(host(acc), oacc, "acc (all rows)")
+    oy = orc.dequant_epilogue(oacc, osx, osw)
+    e = assert_rows_close(bits(y), oy, "y (all rows)")
+    assert_fwd_elementwise(bits(y), oy, "y (all rows)")
     say(f"  max row relerr {e:.2e}")
 
 
