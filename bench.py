@@ -65,11 +65,14 @@ def parse():
     # insensitive to the ramp's tail.
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--only", default="all", choices=["all", "fwd", "copy", "kernels", "ceilings"],
+    ap.add_argument("--only", default="all",
+                    choices=["all", "fwd", "copy", "kernels", "ceilings", "overlap"],
                     help="fwd: headline only; copy: a plain 1 GiB device copy (calibrates "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes); kernels: "
                          "each hot kernel a few times on its workload and the copy, for "
-                         "rocprofv3 kernel traces and counter passes")
+                         "rocprofv3 kernel traces and counter passes; overlap: the forward with "
+                         "the activation quantizer of one row chunk beside the GEMM of the "
+                         "previous one on a second stream, against the two-launch call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -120,6 +123,10 @@ def main():
 
     if args.only == "kernels":
         profile_kernels(cr, torch, dev, wl, to_dev)
+        return
+
+    if args.only == "overlap":
+        print(json.dumps(bench_overlap(cr, torch, dev, wl)), flush=True)
         return
 
     if args.only == "ceilings":
@@ -714,6 +721,88 @@ def bench_packed(cr, torch, dev, dev_normal, time_ms, wl):
     }
     log(f"[bench] packed {r}")
     return r
+
+
+def bench_overlap(cr, torch, dev, wl):
+    """The forward with its two stages overlapped across row chunks: the rows are
+    cut into C chunks; a second stream quantizes chunk c + 1 while the GEMM of
+    chunk c runs, each GEMM waiting on its chunk's quantizer event.  Timed with
+    events on the calling stream against the two-launch call on the same
+    workspace layout, outputs compared bit for bit (same codes, same GEMM)."""
+    def normal(shape, sigma, seed, cols=None):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        v = torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * sigma
+        if cols is not None:
+            v[:, torch.from_numpy(cols).to(dev)] *= wl.OUTLIER_GAIN
+        return v.to(torch.bfloat16)
+
+    def timed(fn, calls=20, min_s=0.1):
+        warm_up(torch, fn, 3, min_s)
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(calls):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / calls * 1e3
+
+    out = {}
+    main_s = torch.cuda.current_stream()
+    qs, gs = torch.cuda.Stream(), torch.cuda.Stream()
+    for name, M, K, N in (("packed_20480x4096x4096", 20480, 4096, 4096),
+                          ("mlp_up_4096x4096x16384", 4096, 4096, 16384)):
+        cols = wl.outlier_columns(K, wl.n_outliers(K), 0)
+        x = normal((M, K), 1.0, 31, cols)
+        qw, sw = cr.quantize_weight(normal((N, K), wl.SIGMA_W, 32))
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(cr.workspace_bytes(cr.OP_LINEAR_FWD, M, N, K), dtype=torch.uint8,
+                         device=dev)
+        qx = torch.empty((M, K), dtype=torch.int8, device=dev)
+        sx = torch.empty((M,), dtype=torch.float32, device=dev)
+        y2 = torch.empty_like(y)
+        base = timed(lambda: cr.linear_fwd(x, qw, sw, out=y, workspace=ws))
+        out[f"{name}_two_launch_us"] = round(base, 1)
+        for C in (2, 4, 5, 8):
+            if M % C or (M // C) % 256:
+                continue
+            R = M // C
+            evs = [torch.cuda.Event() for _ in range(C)]
+
+            def chunked():
+                qs.wait_stream(main_s)
+                gs.wait_stream(main_s)
+                with torch.cuda.stream(qs):
+                    for c in range(C):
+                        cr.quantize_act(x[c * R:(c + 1) * R], out=(qx[c * R:(c + 1) * R],
+                                                                    sx[c * R:(c + 1) * R]))
+                        evs[c].record(qs)
+                with torch.cuda.stream(gs):
+                    for c in range(C):
+                        gs.wait_event(evs[c])
+                        cr.gemm_i8_bf16(qx[c * R:(c + 1) * R], sx[c * R:(c + 1) * R], qw, sw,
+                                        out=y2[c * R:(c + 1) * R])
+                main_s.wait_stream(gs)
+                main_s.wait_stream(qs)
+
+            def serial():
+                for c in range(C):
+                    cr.quantize_act(x[c * R:(c + 1) * R], out=(qx[c * R:(c + 1) * R],
+                                                                sx[c * R:(c + 1) * R]))
+                    cr.gemm_i8_bf16(qx[c * R:(c + 1) * R], sx[c * R:(c + 1) * R], qw, sw,
+                                    out=y2[c * R:(c + 1) * R])
+
+            out[f"{name}_chunks{C}_one_stream_us"] = round(timed(serial), 1)
+            t = timed(chunked)
+            torch.cuda.synchronize()
+            same = bool(torch.equal(y.view(torch.int16), y2.view(torch.int16)))
+            out[f"{name}_chunks{C}_us"] = round(t, 1)
+            out[f"{name}_chunks{C}_bit_identical"] = same
+            log(f"[bench] overlap {name}: two-launch {base:.1f} us, {C} chunks on two streams "
+                f"{t:.1f} us, identical={same}")
+        del x, qw, sw, y, y2, ws, qx, sx
+    return out
 
 
 def bench_text_encoder_quant(cr, torch, dev, dev_normal, wl):
