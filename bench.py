@@ -237,6 +237,8 @@ def main():
     extra["lora16_down_us"] = round(ld_ms * 1e3, 2)
     log(f"[bench] with a rank-16 LoRA branch: {lora_ms * 1e3:.1f} us/call "
         f"(down projection alone {ld_ms * 1e3:.1f} us)")
+    if args.only == "all":
+        extra.update(bench_vs_bf16(cr, torch, time_ms, x, w, qw, sw, ms_step))
     del x, w, ws, y, y2, qx, sx
 
     if args.only == "all":
@@ -291,6 +293,42 @@ def counter_traffic(record, sources, key="hbm_bytes_per_launch"):
     except (OSError, ValueError):
         pass
     return None
+
+
+def bench_vs_bf16(cr, torch, time_ms, x, w, qw, sw, fwd_ms):
+    """The comparison the pages make for the DiT forward (sd-scripts pull request
+    2461, Verification: bf16, the ConvRot int8 path, and the eager fallback that
+    dequantizes and then runs the bf16 GEMM), here for one attention-projection
+    layer on this chip: the vendor bf16 GEMM (torch.mm through hipBLASLt) on the
+    bf16 weight; the fallback as this library's transient dequantization
+    (W_hat^T, bf16) followed by that GEMM; and the fused int8 forward.  Context,
+    not part of the layer."""
+    M, K = x.shape
+    N = w.shape[0]
+    wt = w.t().contiguous()
+    bf16_ms = time_ms(lambda: torch.mm(x, wt), 3, 50)
+    what_t = torch.empty((K, N), dtype=torch.bfloat16, device=x.device)
+
+    def fallback():
+        cr.dequant_weight_t(qw, sw, out=what_t)
+        torch.mm(x, what_t)
+
+    fb_ms = time_ms(fallback, 3, 50)
+    # the same GEMM on the dequantized weight alone (operand data change the
+    # clock the chip holds, so the bf16 weight and W_hat time differently)
+    mm_hat_ms = time_ms(lambda: torch.mm(x, what_t), 3, 50)
+    r = {
+        "vendor_bf16_gemm_4096_us": round(bf16_ms * 1e3, 2),
+        "vendor_bf16_gemm_4096_tflops": round(2.0 * M * N * K / (bf16_ms * 1e-3) / 1e12, 1),
+        "vendor_bf16_gemm_on_w_hat_4096_us": round(mm_hat_ms * 1e3, 2),
+        "dequant_fallback_4096_us": round(fb_ms * 1e3, 2),
+        "fused_int8_over_bf16_time": round(fwd_ms / bf16_ms, 3),
+        "dequant_fallback_over_bf16_time": round(fb_ms / bf16_ms, 3),
+    }
+    log(f"[bench] one 4096^3 layer: bf16 GEMM {bf16_ms * 1e3:.1f} us ({mm_hat_ms * 1e3:.1f} us on "
+        f"W_hat), dequantize + bf16 GEMM {fb_ms * 1e3:.1f} us, fused int8 forward "
+        f"{fwd_ms * 1e3:.1f} us")
+    return r
 
 
 def bench_vendor_int8(torch, dev, time_ms, gemm_us):
