@@ -290,6 +290,31 @@ def test_linear_fwd_tiny(cr, orc):
     assert np.all(np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 1e-30)
 
 
+# the longest contraction the row quantizer takes (CONVROT_MAX_ROW_LEN = 32768):
+# the few-row path (5 rows), the small tiles (300 rows) and the 256 x 256 tiles
+# with a ragged N (2100 rows)
+@pytest.mark.parametrize("M,N,K", [(5, 384, 32768), (300, 640, 32768), (2100, 700, 32768)])
+def test_linear_fwd_max_row_length(cr, orc, M, N, K):
+    say(f"linear_fwd max row length M={M} N={N} K={K}")
+    x = wl.activations(M, K, wl.n_outliers(K), base=M + 1)
+    w = wl.normal_bf16((N, K), wl.SIGMA_W, M + 1, 1)
+    yb, ref = _fwd_case(cr, orc, x, w)
+    assert_rows_close(yb, ref["y"], "y")
+    assert_fwd_elementwise(yb, ref["y"], "y")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 32768, 256), (40, 256, 32768)])
+def test_bwd_max_row_length(cr, orc, M, N, K):
+    # dY rows of the longest length the dY quantizer takes (N = 32768, 16 waves
+    # per row), and an input gradient 32768 wide (the inverse rotation over 256
+    # blocks per row)
+    say(f"bwd max row length M={M} N={N} K={K}")
+    dy = wl.normal_bf16((M, N), wl.SIGMA_DY, N, 3)
+    w = wl.normal_bf16((N, K), wl.SIGMA_W, N, 1)
+    _bwd_int8(cr, orc, dy, w)
+    _bwd_bf16(cr, orc, dy, w)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 8, 128), (5, 130, 256), (300, 260, 384), (257, 1000, 1024)])
 def test_linear_fwd_ragged(cr, orc, M, N, K):
     say(f"linear_fwd ragged M={M} N={N} K={K}")
