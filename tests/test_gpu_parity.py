@@ -315,6 +315,40 @@ def test_bwd_max_row_length(cr, orc, M, N, K):
     _bwd_bf16(cr, orc, dy, w)
 
 
+def test_many_rows(cr, orc):
+    """A million-odd token rows of a short contraction: the row quantizers' and
+    GEMMs' grids at their largest in this suite (over a million rows, tens of
+    thousands of workgroups), checked on seeded sampled rows and both ends."""
+    M, K, N = (1 << 20) + 3, 256, 136
+    say(f"many rows M={M} K={K} N={N}")
+    x = wl.activations(M, K, 3, base=77)
+    w = wl.normal_bf16((N, K), wl.SIGMA_W, 77, 1)
+    qw, sw = cr.quantize_weight(bf16_to_dev(w))
+    xd = bf16_to_dev(x)
+    qx, sx = cr.quantize_act(xd)
+    y = cr.linear_fwd(xd, qw, sw)
+    rows = np.unique(np.concatenate([[0, 1, M - 2, M - 1],
+                                     np.random.default_rng(77).choice(M, 500, False)]))
+    oqw, osw, _ = orc.rotate_quantize(w)
+    oqx, osx, _ = orc.rotate_quantize(x[rows])
+    rows_t = torch.from_numpy(rows).cuda()
+    assert_exact(host(qx[rows_t]), oqx, "q_x (sampled rows)")
+    assert_exact(host(sx[rows_t]), osx, "s_x (sampled rows)")
+    oy = orc.dequant_epilogue(orc.gemm_i8_i32(oqx, oqw), osx, osw)
+    assert_rows_close(bits(y[rows_t]), oy, "y (sampled rows)")
+    assert_fwd_elementwise(bits(y[rows_t]), oy, "y (sampled rows)")
+    # both input gradients through dY rows of 128 values (N = 128)
+    w2 = wl.normal_bf16((128, K), wl.SIGMA_W, 78, 1)
+    dy = wl.normal_bf16((M, 128), wl.SIGMA_DY, 78, 3)
+    qw2, sw2 = cr.quantize_weight(bf16_to_dev(w2))
+    oqw2, osw2, _ = orc.rotate_quantize(w2)
+    dyd = bf16_to_dev(dy)
+    for mode, ref in ((cr.BWD_INT8, orc.bwd_dx_int8), (cr.BWD_BF16, orc.bwd_dx_bf16)):
+        dx = cr.linear_bwd_dx(dyd, qw2, sw2, mode)
+        assert_rows_close(bits(dx[rows_t]), ref(dy[rows], oqw2, osw2)["dx"], f"dX mode {mode}")
+    del xd, dyd
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 8, 128), (5, 130, 256), (300, 260, 384), (257, 1000, 1024)])
 def test_linear_fwd_ragged(cr, orc, M, N, K):
     say(f"linear_fwd ragged M={M} N={N} K={K}")
