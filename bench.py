@@ -301,33 +301,44 @@ def bench_vs_bf16(cr, torch, time_ms, x, w, qw, sw, fwd_ms):
     dequantizes and then runs the bf16 GEMM), here for one attention-projection
     layer on this chip: the vendor bf16 GEMM (torch.mm through hipBLASLt) on the
     bf16 weight; the fallback as this library's transient dequantization
-    (W_hat^T, bf16) followed by that GEMM; and the fused int8 forward.  Context,
-    not part of the layer."""
+    (W_hat^T, bf16) followed by that GEMM; and the fused int8 forward.  Device
+    times from graph replays: called eagerly, torch.mm spends more time on the
+    host than its kernel takes, which would leave the GPU idle between calls.
+    Context, not part of the layer."""
     M, K = x.shape
     N = w.shape[0]
     wt = w.t().contiguous()
-    bf16_ms = time_ms(lambda: torch.mm(x, wt), 3, 50)
-    what_t = torch.empty((K, N), dtype=torch.bfloat16, device=x.device)
+    what_t = cr.dequant_weight_t(qw, sw)
+    yb = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    ws = torch.empty(cr.workspace_bytes(cr.OP_LINEAR_FWD, M, N, K), dtype=torch.uint8,
+                     device=x.device)
 
     def fallback():
         cr.dequant_weight_t(qw, sw, out=what_t)
-        torch.mm(x, what_t)
+        torch.mm(x, what_t, out=yb)
 
-    fb_ms = time_ms(fallback, 3, 50)
+    bf16_ms = time_graph_ms(torch, lambda: torch.mm(x, wt, out=yb))
     # the same GEMM on the dequantized weight alone (operand data change the
     # clock the chip holds, so the bf16 weight and W_hat time differently)
-    mm_hat_ms = time_ms(lambda: torch.mm(x, what_t), 3, 50)
+    mm_hat_ms = time_graph_ms(torch, lambda: torch.mm(x, what_t, out=yb))
+    fb_ms = time_graph_ms(torch, fallback)
+    int8_ms = time_graph_ms(torch, lambda: cr.linear_fwd(x, qw, sw, out=y, workspace=ws))
+    eager_ms = time_ms(lambda: torch.mm(x, wt, out=yb), 3, 50)
     r = {
         "vendor_bf16_gemm_4096_us": round(bf16_ms * 1e3, 2),
         "vendor_bf16_gemm_4096_tflops": round(2.0 * M * N * K / (bf16_ms * 1e-3) / 1e12, 1),
+        "vendor_bf16_gemm_4096_eager_us": round(eager_ms * 1e3, 2),
         "vendor_bf16_gemm_on_w_hat_4096_us": round(mm_hat_ms * 1e3, 2),
         "dequant_fallback_4096_us": round(fb_ms * 1e3, 2),
-        "fused_int8_over_bf16_time": round(fwd_ms / bf16_ms, 3),
+        "fused_int8_fwd_graph_us": round(int8_ms * 1e3, 2),
+        "fused_int8_over_bf16_time": round(int8_ms / bf16_ms, 3),
         "dequant_fallback_over_bf16_time": round(fb_ms / bf16_ms, 3),
     }
-    log(f"[bench] one 4096^3 layer: bf16 GEMM {bf16_ms * 1e3:.1f} us ({mm_hat_ms * 1e3:.1f} us on "
-        f"W_hat), dequantize + bf16 GEMM {fb_ms * 1e3:.1f} us, fused int8 forward "
-        f"{fwd_ms * 1e3:.1f} us")
+    log(f"[bench] one 4096^3 layer, device time: bf16 GEMM {bf16_ms * 1e3:.1f} us "
+        f"({mm_hat_ms * 1e3:.1f} us on W_hat; {eager_ms * 1e3:.1f} us per eager call), "
+        f"dequantize + bf16 GEMM {fb_ms * 1e3:.1f} us, fused int8 forward {int8_ms * 1e3:.1f} us "
+        f"({fwd_ms * 1e3:.1f} us eager)")
     return r
 
 
