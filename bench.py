@@ -319,8 +319,7 @@ def bench_vs_bf16(cr, torch, time_ms, x, w, qw, sw, fwd_ms):
         torch.mm(x, what_t, out=yb)
 
     bf16_ms = time_graph_ms(torch, lambda: torch.mm(x, wt, out=yb))
-    # the same GEMM on the dequantized weight alone (operand data change the
-    # clock the chip holds, so the bf16 weight and W_hat time differently)
+    # the same GEMM on the dequantized weight alone (the fallback's GEMM)
     mm_hat_ms = time_graph_ms(torch, lambda: torch.mm(x, what_t, out=yb))
     fb_ms = time_graph_ms(torch, fallback)
     int8_ms = time_graph_ms(torch, lambda: cr.linear_fwd(x, qw, sw, out=y, workspace=ws))
